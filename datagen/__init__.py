@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs for the fused chunked top-K KL distillation loss.
+
+This module serves both the fp64 oracle and the HIP path. It holds none of the
+loss's arithmetic: it only draws hidden states, an output head, a top-K teacher
+cache (ids + logits) and a position mask with the shapes and value
+distributions of the workloads below, and converts fp32 draws to bfloat16 bit
+patterns (numpy has no bfloat16; both sides read the same uint16 bits).
+
+Workloads (each a synthetic stand-in for the student output projection the
+pages measure; the pages use no public dataset for the loss benchmark:
+Glonce, "Multiverse Computing cuts LLM distillation VRAM by 15x with chunked
+KL loss", paragraph on the isolated output-projection benchmark):
+
+  1 tiny-fp32    T=512    d=256  V=4096   K=16  chunk=128  tau=1  fp32 inputs
+  2 llama3b-8k   T=8192   d=3072 V=128256 K=100 chunk=1024 tau=1  bf16
+  3 gptoss-32k   T=32768  d=2880 V=201088 K=100 chunk=2048 tau=1  bf16
+  4 long-128k    T=131072 d=2880 V=201088 K=100 chunk=4096 tau=2  bf16
+  5 extreme-256k T=262144 d=2880 V=201088 K=100 chunk=4096 tau=1  bf16
+
+K=100 follows the top-100 teacher cache (Glonce, same page, paragraph on
+Multiverse's two-part fix; ainewsbank, "Multiverse Computing Tests
+Lower-Memory Long-Context Distillation", section "Two changes remove
+different bottlenecks"). V=201,088 is the gpt-oss vocabulary the pages quote
+(epoka.news, "Two systems changes ...", section "Where the memory goes").
+
+Draw recipe (numpy PCG64, SeedSequence(seed).spawn(7) in the fixed order
+hidden, W, idx, logit, mask, overlap-rows, peaked-rows):
+  hidden  cfg1: N(0,1) fp32.  cfg2-5: N(0,1) per element, each row divided by
+          sqrt(mean(x^2)+1e-6) (RMS-normalised), then rounded to bf16 (RNE).
+  W       cfg1: N(0, variance 1/d) fp32.  cfg2-5: N(0, std 0.02) -> bf16.
+  idx     K distinct ids per row, uniform over [0, V) (rows with a repeated
+          id are redrawn until distinct).  cfg2-5: rows chosen by
+          Bernoulli(0.3) instead take the student's own top-K ids under the
+          generated W, i.e. the K largest of z = h_bf16 . W_bf16^T computed in
+          fp32, ordered by descending z (ties: lower id first).
+  logit   cfg1: N(0, std 2).  cfg2-5: N(0, std 3).  Each row sorted
+          descending.  cfg4: rows chosen by Bernoulli(0.1) get logit[:,0] += 8.
+  mask    uint8, 1 = position counts; each position is 0 with probability
+          0.05 (0.02 for cfg5).
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+__all__ = ["Config", "CONFIGS", "make_inputs", "f32_to_bf16_bits",
+           "bf16_bits_to_f32", "config_for"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Shape and distribution parameters of one synthetic workload."""
+    num: int
+    name: str
+    T: int
+    d: int
+    V: int
+    K: int
+    chunk: int
+    tau: float
+    dtype: str            # "f32" or "bf16" for hidden and W
+    mask_zero_p: float
+    hidden_rms_norm: bool
+    w_std: float | None   # None -> variance 1/d
+    logit_std: float
+    overlap_p: float      # fraction of rows whose ids are the student's top-K
+    peaked_p: float       # fraction of rows whose top logit gets +8
+
+
+CONFIGS = {
+    1: Config(1, "tiny-fp32", 512, 256, 4096, 16, 128, 1.0, "f32", 0.05,
+              False, None, 2.0, 0.0, 0.0),
+    2: Config(2, "llama3b-8k", 8192, 3072, 128256, 100, 1024, 1.0, "bf16",
+              0.05, True, 0.02, 3.0, 0.3, 0.0),
+    3: Config(3, "gptoss-32k", 32768, 2880, 201088, 100, 2048, 1.0, "bf16",
+              0.05, True, 0.02, 3.0, 0.3, 0.0),
+    4: Config(4, "long-128k", 131072, 2880, 201088, 100, 4096, 2.0, "bf16",
+              0.05, True, 0.02, 3.0, 0.3, 0.1),
+    5: Config(5, "extreme-256k", 262144, 2880, 201088, 100, 4096, 1.0, "bf16",
+              0.02, True, 0.02, 3.0, 0.3, 0.0),
+}
+
+
+def config_for(num: int, **overrides) -> Config:
+    """Return workload `num`, optionally with fields replaced (e.g. T=600)."""
+    return dataclasses.replace(CONFIGS[num], **overrides)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bfloat16 (round to nearest, ties to even); uint16 bits.
+
+    Inputs are finite by construction here, so NaN handling is not needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to fp32 exactly."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def _distinct_ids(rng: np.random.Generator, T: int, K: int, V: int) -> np.ndarray:
+    ids = rng.integers(0, V, size=(T, K), dtype=np.int64)
+    while True:
+        s = np.sort(ids, axis=1)
+        bad = np.nonzero((s[:, 1:] == s[:, :-1]).any(axis=1))[0]
+        if bad.size == 0:
+            return ids.astype(np.int32)
+        ids[bad] = rng.integers(0, V, size=(bad.size, K), dtype=np.int64)
+
+
+def _student_topk_rows(h_f32: np.ndarray, w_f32: np.ndarray, K: int,
+                       backend: str = "numpy", block: int = 256) -> np.ndarray:
+    """K largest entries of h . W^T per row (fp32), descending, ties by id."""
+    out = np.empty((h_f32.shape[0], K), dtype=np.int32)
+    if backend == "torch-cuda":
+        import torch
+        wt = torch.from_numpy(w_f32).cuda()
+        for r0 in range(0, h_f32.shape[0], 4096):
+            z = torch.from_numpy(h_f32[r0:r0 + 4096]).cuda() @ wt.T
+            # torch.topk returns values in descending order; re-sort on the
+            # host with the id tie-break so both backends order ties alike.
+            vals, ids = torch.topk(z, K, dim=1)
+            vals = vals.cpu().numpy()
+            ids = ids.cpu().numpy()
+            order = np.lexsort((ids, -vals), axis=1)
+            out[r0:r0 + 4096] = np.take_along_axis(ids, order, axis=1)
+        return out
+    for r0 in range(0, h_f32.shape[0], block):
+        z = h_f32[r0:r0 + block] @ w_f32.T
+        part = np.argpartition(-z, K - 1, axis=1)[:, :K]
+        vals = np.take_along_axis(z, part, axis=1)
+        order = np.lexsort((part, -vals), axis=1)
+        out[r0:r0 + block] = np.take_along_axis(part, order, axis=1)
+    return out
+
+
+def make_inputs(cfg: Config | int, seed: int = 0, topk_backend: str = "numpy",
+                **overrides) -> dict:
+    """Draw one workload's inputs.
+
+    Returns a dict with hidden [T,d], W [V,d] (float32 for dtype "f32", uint16
+    bfloat16 bits for "bf16"), teacher_idx [T,K] int32, teacher_logit [T,K]
+    float32, mask [T] uint8 (1 = counts), and tau, chunk, dtype, cfg.
+    """
+    if isinstance(cfg, int):
+        cfg = CONFIGS[cfg]
+    if overrides:
+        cfg = dataclasses.replace(cfg, **overrides)
+    T, d, V, K = cfg.T, cfg.d, cfg.V, cfg.K
+    ss = np.random.SeedSequence(seed).spawn(7)
+    r_h, r_w, r_idx, r_logit, r_mask, r_ovl, r_peak = (
+        np.random.Generator(np.random.PCG64(s)) for s in ss)
+
+    h = r_h.standard_normal((T, d), dtype=np.float32)
+    if cfg.hidden_rms_norm:
+        ms = np.mean(h.astype(np.float64) ** 2, axis=1, keepdims=True)
+        h = (h / np.sqrt(ms + 1e-6)).astype(np.float32)
+    w_std = cfg.w_std if cfg.w_std is not None else 1.0 / np.sqrt(d)
+    w = (r_w.standard_normal((V, d), dtype=np.float32) * np.float32(w_std))
+
+    idx = _distinct_ids(r_idx, T, K, V)
+    logit = r_logit.standard_normal((T, K), dtype=np.float32) * np.float32(cfg.logit_std)
+    logit = -np.sort(-logit, axis=1)
+    mask = (r_mask.random(T) >= cfg.mask_zero_p).astype(np.uint8)
+
+    if cfg.dtype == "bf16":
+        hidden = f32_to_bf16_bits(h)
+        W = f32_to_bf16_bits(w)
+    else:
+        hidden, W = h, w
+
+    if cfg.overlap_p > 0:
+        rows = np.nonzero(r_ovl.random(T) < cfg.overlap_p)[0]
+        if rows.size:
+            hf = bf16_bits_to_f32(hidden[rows]) if cfg.dtype == "bf16" else hidden[rows]
+            wf = bf16_bits_to_f32(W) if cfg.dtype == "bf16" else W
+            idx[rows] = _student_topk_rows(hf, wf, K, topk_backend)
+    if cfg.peaked_p > 0:
+        rows = np.nonzero(r_peak.random(T) < cfg.peaked_p)[0]
+        logit[rows, 0] += np.float32(8.0)
+
+    return dict(hidden=np.ascontiguousarray(hidden), W=np.ascontiguousarray(W),
+                teacher_idx=np.ascontiguousarray(idx),
+                teacher_logit=np.ascontiguousarray(logit), mask=mask,
+                tau=float(cfg.tau), chunk=int(cfg.chunk), dtype=cfg.dtype,
+                cfg=cfg)
