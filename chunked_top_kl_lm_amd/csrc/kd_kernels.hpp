@@ -1,0 +1,443 @@
+// kd_kernels.hpp -- epilogues of the shared GEMM and the small kernels of the
+// fused chunked top-K KL loss (gfx950).
+//
+// Notation: a chunk holds rows t in [0, R) of the sequence (global row
+// c0 + t); S = z / tau; statistics over the vocabulary are kept in base 2,
+// x2 = z * log2(e) / tau, so that exp2 / log2 map to v_exp_f32 / v_log_f32.
+#pragma once
+
+#include "kd_gemm.hpp"
+#include <math.h>
+
+namespace kd {
+
+constexpr int kMaxK = 4096;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// GEMM epilogues
+// ---------------------------------------------------------------------------
+
+// Forward pass of a chunk: per (vocabulary strip of one wave, row t) the
+// running max and sum of exp2 -- the partial logsumexp that the online merge
+// folds into the row's full-vocabulary normaliser.  The logits themselves are
+// never written (the chunk is "folded into the running loss and discarded":
+// Glonce, "Multiverse Computing cuts LLM distillation VRAM by 15x with
+// chunked KL loss", paragraph on Multiverse's two-part fix).
+struct EpiLsePartial {
+  float2* part;   // [nvt][ldp]: (max x2, sum exp2(x2 - max)) per strip and row
+  int ldp;
+  int V;
+  float c2;       // log2(e) / tau
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    const int vt = c.m0 / (FM * 32);
+    const bool full = c.m0 + FM * 32 <= V;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = c.m0 + 32 * i + acc_row(r, c.lane);
+          if (full || v < V) mx = fmaxf(mx, acc[i][j][r] * c2);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float sm = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = c.m0 + 32 * i + acc_row(r, c.lane);
+            if (full || v < V) sm += fast_exp2(acc[i][j][r] * c2 - mx);
+          }
+      }
+      sm += __shfl_xor(sm, 32);
+      if (c.lane < 32) part[(int64_t)vt * ldp + c.n0 + 32 * j + c.lane] = make_float2(mx, sm);
+    }
+  }
+};
+
+// Backward recompute of a chunk: the logit gradient of the loss,
+// G[t,v] = (tau/N) m_t q[t,v], written in two layouts (G [R_p][V_p] and
+// G^T [V_p][R_p]) for the two gradient GEMMs.  The sparse teacher part
+// -(tau/N) m_t P[t,v] is subtracted afterwards by scatter_sparse_kernel.
+template <class E>
+struct EpiGrad {
+  typename E::T* G;
+  int64_t ldg;
+  typename E::T* Gt;
+  int64_t ldgt;
+  const float* lse2;      // [R] row normaliser in base 2
+  const uint8_t* mask;    // chunk rows, or nullptr
+  const int* count;       // N
+  float tau, c2;
+  int V, R;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    const int N = *count;
+    const float s = N > 0 ? tau / (float)N : 0.f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = c.n0 + 32 * j + acc_col(c.lane);
+      float sc = 0.f, l2 = 0.f;
+      if (n < R) {
+        if (!mask || mask[n]) sc = s;
+        l2 = lse2[n];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int v0 = c.m0 + 32 * i + 8 * g4 + 4 * (c.lane >> 5);
+          float gv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = acc[i][j][4 * g4 + e];
+            gv[e] = (sc != 0.f && v0 + e < V) ? sc * fast_exp2(x * c2 - l2) : 0.f;
+          }
+          store4(G + (int64_t)n * ldg + v0, gv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Gt[(int64_t)(v0 + e) * ldgt + n] = store_cvt<E>(gv[e]);
+        }
+    }
+  }
+
+  __device__ __forceinline__ static void store4(uint16_t* p, const float* g) {
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16(g[0]) | ((uint32_t)f32_to_bf16(g[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(g[2]) | ((uint32_t)f32_to_bf16(g[3]) << 16);
+    *(uint2*)p = w;
+  }
+  __device__ __forceinline__ static void store4(float* p, const float* g) {
+    *(float4*)p = make_float4(g[0], g[1], g[2], g[3]);
+  }
+};
+
+// Split-K partial of the hidden gradient: plain fp32 tile store into
+// out[split][m][n] (the partials are summed in a fixed order afterwards).
+struct EpiStoreSplit {
+  float* out;
+  int64_t ld;
+  int64_t split_stride;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    float* base = out + (int64_t)c.split * split_stride;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = c.m0 + 32 * i + acc_row(r, c.lane);
+          const int n = c.n0 + 32 * j + acc_col(c.lane);
+          base[(int64_t)m * ld + n] = acc[i][j][r];
+        }
+  }
+};
+
+// Head gradient: grad_W[v][j] (+)= tile, accumulated across chunks in fp32
+// (the first chunk stores).
+struct EpiAccum {
+  float* out;
+  int64_t ld;
+  int M, N;
+  int first;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = c.n0 + 32 * j + acc_col(c.lane);
+        if (n >= N) continue;
+        float old[16];
+        if (!first) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = c.m0 + 32 * i + acc_row(r, c.lane);
+            old[r] = m < M ? out[(int64_t)m * ld + n] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = c.m0 + 32 * i + acc_row(r, c.lane);
+          if (m < M) out[(int64_t)m * ld + n] = first ? acc[i][j][r] : old[r] + acc[i][j][r];
+        }
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Block reductions (fixed order: deterministic)
+// ---------------------------------------------------------------------------
+
+template <int NT, class T, class Op>
+__device__ __forceinline__ T block_reduce(T v, T* s_buf, Op op) {
+  const int tid = threadIdx.x;
+  s_buf[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int w = NT / 2; w > 0; w >>= 1) {
+    if (tid < w) s_buf[tid] = op(s_buf[tid], s_buf[tid + w]);
+    __syncthreads();
+  }
+  T r = s_buf[0];
+  __syncthreads();
+  return r;
+}
+
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpAddF { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpAddD { __device__ double operator()(double a, double b) const { return a + b; } };
+struct OpAddI { __device__ int operator()(int a, int b) const { return a + b; } };
+
+// Teacher distribution of one row: a_k = logit_k / tau kept in s_a, and the
+// log normaliser log sum_k exp(a_k).  p_k = exp(a_k - lse_a).  Used by both
+// the KL kernel and the sparse scatter so that both see the same p.
+template <int NT>
+__device__ __forceinline__ float teacher_row(const float* logit_row, int K, float inv_tau,
+                                             float* s_a, float* s_red) {
+  float mx = -INFINITY;
+  for (int k = threadIdx.x; k < K; k += NT) {
+    const float a = logit_row[k] * inv_tau;
+    s_a[k] = a;
+    mx = fmaxf(mx, a);
+  }
+  mx = block_reduce<NT>(mx, s_red, OpMax());
+  float sm = 0.f;
+  for (int k = threadIdx.x; k < K; k += NT) sm += expf(s_a[k] - mx);
+  sm = block_reduce<NT>(sm, s_red, OpAddF());
+  return mx + logf(sm);
+}
+
+// ---------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------
+
+// N = number of counted positions; clears the loss accumulator and status.
+__global__ __launch_bounds__(1024) void prep_kernel(const uint8_t* mask, int64_t T, int* count,
+                                                    double* loss_acc, int32_t* status) {
+  __shared__ int s_red[1024];
+  int c = 0;
+  for (int64_t t = threadIdx.x; t < T; t += 1024) c += mask ? (mask[t] != 0) : 1;
+  c = block_reduce<1024>(c, s_red, OpAddI());
+  if (threadIdx.x == 0) {
+    *count = c;
+    *loss_acc = 0.0;
+    if (status) *status = 0;
+  }
+}
+
+// dst[c][r] = src[r][c] for r < rows, c < cols; zero elsewhere in the
+// [dst_rows x ld_dst] destination.  64x64 tiles through LDS.
+template <class E>
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const typename E::T* src, int64_t ld_src,
+                                                            int64_t rows, int64_t cols,
+                                                            typename E::T* dst, int64_t ld_dst) {
+  typedef typename E::T T;
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? src[r * ld_src + c] : (T)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    dst[c * ld_dst + r] = tile[tx][i];
+  }
+}
+
+// dst[r][c] = src[r][c] for r < rows, c < cols; zero elsewhere in the
+// [dst_rows x ld_dst] destination.
+template <class E>
+__global__ __launch_bounds__(256) void pad_kernel(const typename E::T* src, int64_t ld_src, int64_t rows,
+                                                  int64_t cols, typename E::T* dst, int64_t ld_dst,
+                                                  int64_t dst_rows) {
+  typedef typename E::T T;
+  const int64_t n = dst_rows * ld_dst;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / ld_dst, c = i - r * ld_dst;
+    dst[i] = (r < rows && c < cols) ? src[r * ld_src + c] : (T)0;
+  }
+}
+
+template <class E> __device__ __forceinline__ float dot16(u32x4 a, u32x4 b);
+template <> __device__ __forceinline__ float dot16<Bf16>(u32x4 a, u32x4 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16);
+    s += __uint_as_float(a[i] & 0xffff0000u) * __uint_as_float(b[i] & 0xffff0000u);
+  }
+  return s;
+}
+template <> __device__ __forceinline__ float dot16<F32>(u32x4 a, u32x4 b) {
+  f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+  return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+}
+
+// One block per chunk row t:
+//  1. merge the per-strip (max, sum) partials into the row's logsumexp
+//     (online logsumexp across vocabulary tiles);
+//  2. the teacher's distribution p over its K cached ids;
+//  3. the student logits at those ids, z_k = h_t . W[idx_k] (gathered rows);
+//  4. KL_t = sum_k p_k (log p_k - (z_k / tau - LSE_t)).
+// Invalid ids set *status and contribute nothing.
+template <class E>
+__global__ __launch_bounds__(256) void kl_rows_kernel(
+    const float2* part, int ldp, int nvt,
+    const typename E::T* hsrc, int64_t ldh, const typename E::T* wsrc, int64_t ldw, int units16,
+    const int32_t* idx, const float* logit, int K, int V, float tau,
+    float* lse2_out, double* rowkl, float* row_lse, float* row_kl, int32_t* status) {
+  __shared__ float s_a[kMaxK];
+  __shared__ float s_z[kMaxK];
+  __shared__ float s_m[256];
+  __shared__ float s_l[256];
+  __shared__ double s_d[256];
+  const int t = blockIdx.x, tid = threadIdx.x;
+
+  // 1. online merge of the vocabulary-strip partials (fixed order)
+  float M = -INFINITY, L = 0.f;
+  for (int vt = tid; vt < nvt; vt += 256) {
+    const float2 p = part[(int64_t)vt * ldp + t];
+    if (p.x == -INFINITY) continue;
+    if (p.x > M) { L = L * fast_exp2(M - p.x) + p.y; M = p.x; }
+    else L += p.y * fast_exp2(p.x - M);
+  }
+  s_m[tid] = M; s_l[tid] = L;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      const float m1 = s_m[tid], l1 = s_l[tid], m2 = s_m[tid + w], l2 = s_l[tid + w];
+      const float mm = fmaxf(m1, m2);
+      float ll = 0.f;
+      if (mm != -INFINITY) {
+        ll = (m1 == -INFINITY ? 0.f : l1 * fast_exp2(m1 - mm)) + (m2 == -INFINITY ? 0.f : l2 * fast_exp2(m2 - mm));
+      }
+      s_m[tid] = mm; s_l[tid] = ll;
+    }
+    __syncthreads();
+  }
+  const float lse2 = s_m[0] + __log2f(s_l[0]);
+  const float lse = lse2 * kLn2;   // natural-log normaliser of S = z / tau
+  __syncthreads();
+
+  // 2. teacher distribution over the K ids
+  const float inv_tau = 1.f / tau;
+  const float lse_a = teacher_row<256>(logit + (int64_t)t * K, K, inv_tau, s_a, s_m);
+
+  // 3. gathered student logits at the teacher ids
+  const int lane = tid & 63, wid = tid >> 6;
+  const u32x4* h = (const u32x4*)(hsrc + (int64_t)t * ldh);
+  for (int k = wid; k < K; k += 4) {
+    const int id = idx[(int64_t)t * K + k];
+    float dot = 0.f;
+    const bool ok = id >= 0 && id < V;
+    if (ok) {
+      const u32x4* w = (const u32x4*)(wsrc + (int64_t)id * ldw);
+      for (int u = lane; u < units16; u += 64) dot += dot16<E>(h[u], w[u]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    if (lane == 0) {
+      s_z[k] = ok ? dot : NAN;
+      if (!ok && status) *status = 7;  // KD_ERR_BAD_INDEX
+    }
+  }
+  __syncthreads();
+
+  // 4. KL_t
+  double kl = 0.0;
+  for (int k = tid; k < K; k += 256) {
+    const float z = s_z[k];
+    if (z != z) continue;                     // invalid id: no contribution
+    const float logp = s_a[k] - lse_a;
+    const float p = expf(logp);
+    if (p > 0.f) kl += (double)p * ((double)logp - ((double)z * inv_tau - (double)lse));
+  }
+  kl = block_reduce<256>(kl, s_d, OpAddD());
+  if (tid == 0) {
+    rowkl[t] = kl;
+    lse2_out[t] = lse2;
+    if (row_lse) row_lse[t] = lse;
+    if (row_kl) row_kl[t] = (float)kl;
+  }
+}
+
+// loss_acc += sum_t m_t KL_t over the chunk, fixed order, fp64.
+__global__ __launch_bounds__(256) void chunk_loss_kernel(const double* rowkl, const uint8_t* mask, int R,
+                                                         double* loss_acc) {
+  __shared__ double s_d[256];
+  double s = 0.0;
+  for (int t = threadIdx.x; t < R; t += 256)
+    if (!mask || mask[t]) s += rowkl[t];
+  s = block_reduce<256>(s, s_d, OpAddD());
+  if (threadIdx.x == 0) *loss_acc += s;
+}
+
+// Sparse teacher part of the logit gradient: G[t, id] -= (tau/N) m_t P[t, id]
+// for every distinct valid id of the row (duplicates summed first), in both
+// gradient layouts.  One block per chunk row.
+template <class E>
+__global__ __launch_bounds__(128) void scatter_sparse_kernel(
+    const int32_t* idx, const float* logit, const uint8_t* mask, int K, int V, float tau,
+    const int* count, typename E::T* G, int64_t ldg, typename E::T* Gt, int64_t ldgt) {
+  __shared__ float s_a[kMaxK];
+  __shared__ int s_id[kMaxK];
+  __shared__ float s_red[128];
+  const int t = blockIdx.x;
+  const int N = *count;
+  if (N == 0 || (mask && !mask[t])) return;
+  const float s = tau / (float)N;
+  const float inv_tau = 1.f / tau;
+  for (int k = threadIdx.x; k < K; k += 128) s_id[k] = idx[(int64_t)t * K + k];
+  const float lse_a = teacher_row<128>(logit + (int64_t)t * K, K, inv_tau, s_a, s_red);
+  __syncthreads();
+  for (int k = threadIdx.x; k < K; k += 128) {
+    const int id = s_id[k];
+    if (id < 0 || id >= V) continue;
+    bool first = true;
+    for (int k2 = 0; k2 < k; ++k2)
+      if (s_id[k2] == id) { first = false; break; }
+    if (!first) continue;
+    float P = 0.f;
+    for (int k2 = k; k2 < K; ++k2)
+      if (s_id[k2] == id) P += expf(s_a[k2] - lse_a);
+    typename E::T* g = G + (int64_t)t * ldg + id;
+    const typename E::T nv = store_cvt<E>(load_elem<E>(g) - s * P);
+    *g = nv;
+    Gt[(int64_t)id * ldgt + t] = nv;
+  }
+}
+
+// grad_hidden rows of the chunk: fixed-order sum of the split-K partials.
+__global__ __launch_bounds__(256) void dh_reduce_kernel(const float* part, int64_t ldp, int64_t split_stride,
+                                                        int splits, int R, int d, float* out, int64_t ldo) {
+  const int64_t n = (int64_t)R * d;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / d, j = i - t * d;
+    const float* p = part + t * ldp + j;
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += p[(int64_t)sp * split_stride];
+    out[t * ldo + j] = s;
+  }
+}
+
+__global__ void finalize_kernel(const double* loss_acc, const int* count, float tau, float* loss) {
+  const int N = *count;
+  *loss = N > 0 ? (float)((double)tau * (double)tau * (*loss_acc) / (double)N) : 0.f;
+}
+
+}  // namespace kd

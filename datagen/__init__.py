@@ -41,6 +41,8 @@ hidden, W, idx, logit, mask, overlap-rows, peaked-rows):
 from __future__ import annotations
 
 import dataclasses
+import functools
+
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "make_inputs", "f32_to_bf16_bits",
@@ -102,6 +104,33 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
             << np.uint32(16)).view(np.float32)
 
 
+@functools.lru_cache(maxsize=1)
+def _draw_w_cached(entropy, spawn_key, V, d, w_std):
+    r_w = np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence(entropy, spawn_key=spawn_key)))
+    std = w_std if w_std is not None else 1.0 / np.sqrt(d)
+    w = r_w.standard_normal((V, d), dtype=np.float32) * np.float32(std)
+    w.setflags(write=False)
+    return w
+
+
+def _draw_w(seq, V, d, w_std):
+    """The head W depends only on (seed, V, d, std): configs 3-5 share it, so
+    the last draw is cached (read-only)."""
+    return _draw_w_cached(seq.entropy, seq.spawn_key, V, d, w_std)
+
+
+@functools.lru_cache(maxsize=1)
+def _w_bits_cached(entropy, spawn_key, V, d, w_std):
+    b = f32_to_bf16_bits(_draw_w_cached(entropy, spawn_key, V, d, w_std))
+    b.setflags(write=False)
+    return b
+
+
+def _w_bits(seq, V, d, w_std):
+    return _w_bits_cached(seq.entropy, seq.spawn_key, V, d, w_std)
+
+
 def _distinct_ids(rng: np.random.Generator, T: int, K: int, V: int) -> np.ndarray:
     ids = rng.integers(0, V, size=(T, K), dtype=np.int64)
     while True:
@@ -159,8 +188,7 @@ def make_inputs(cfg: Config | int, seed: int = 0, topk_backend: str = "numpy",
     if cfg.hidden_rms_norm:
         ms = np.mean(h.astype(np.float64) ** 2, axis=1, keepdims=True)
         h = (h / np.sqrt(ms + 1e-6)).astype(np.float32)
-    w_std = cfg.w_std if cfg.w_std is not None else 1.0 / np.sqrt(d)
-    w = (r_w.standard_normal((V, d), dtype=np.float32) * np.float32(w_std))
+    w = _draw_w(ss[1], V, d, cfg.w_std)
 
     idx = _distinct_ids(r_idx, T, K, V)
     logit = r_logit.standard_normal((T, K), dtype=np.float32) * np.float32(cfg.logit_std)
@@ -169,7 +197,7 @@ def make_inputs(cfg: Config | int, seed: int = 0, topk_backend: str = "numpy",
 
     if cfg.dtype == "bf16":
         hidden = f32_to_bf16_bits(h)
-        W = f32_to_bf16_bits(w)
+        W = _w_bits(ss[1], V, d, cfg.w_std)
     else:
         hidden, W = h, w
 
@@ -183,7 +211,7 @@ def make_inputs(cfg: Config | int, seed: int = 0, topk_backend: str = "numpy",
         rows = np.nonzero(r_peak.random(T) < cfg.peaked_p)[0]
         logit[rows, 0] += np.float32(8.0)
 
-    return dict(hidden=np.ascontiguousarray(hidden), W=np.ascontiguousarray(W),
+    return dict(hidden=np.ascontiguousarray(hidden), W=W,
                 teacher_idx=np.ascontiguousarray(idx),
                 teacher_logit=np.ascontiguousarray(logit), mask=mask,
                 tau=float(cfg.tau), chunk=int(cfg.chunk), dtype=cfg.dtype,

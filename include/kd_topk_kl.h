@@ -1,0 +1,128 @@
+/*
+ * kd_topk_kl.h -- C ABI of the fused chunked top-K KL distillation loss on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A student's hidden states are projected through its output
+ * head one sequence chunk at a time; each chunk's full-vocabulary logits are
+ * folded into the running loss and discarded, and the backward pass
+ * recomputes each chunk instead of storing the sequence x vocabulary grid
+ * (Glonce, "Multiverse Computing cuts LLM distillation VRAM by 15x with
+ * chunked KL loss", paragraph on Multiverse's two-part fix).  The teacher is
+ * represented by an offline cache of its K largest logits per position
+ * (same paragraph: top-100; epoka.news, "Two systems changes that cut the
+ * cost of knowledge distillation", section "The two proposed changes").
+ *
+ * The pages give no formula; the loss computed here is, with S = z / tau and
+ * z = h W^T over the whole vocabulary V:
+ *   p[t,k]  = softmax over the K cached ids of teacher_logit[t,:] / tau
+ *   log q   = S[t,:] - logsumexp_v S[t,:]
+ *   KL_t    = sum_k p[t,k] (log p[t,k] - log q[t, teacher_idx[t,k]])
+ *   loss    = tau^2 * sum_t m_t KL_t / N,   N = #positions with mask != 0
+ * and the outputs are its exact gradients: with
+ *   G[t,v] = (tau/N) m_t (q[t,v] - P[t,v]),  P[t,v] = sum_k p[t,k][idx=v]
+ * (duplicate ids add), grad_hidden = G W and grad_W = G^T H.  N = 0 gives
+ * loss 0 and zero gradients.
+ *
+ * Conventions for every entry point below.
+ *  - Pointers named as device pointers are device memory owned by the
+ *    caller.  The library allocates no device memory, keeps no pointer after
+ *    a call returns and holds no global state.  Calls on different streams
+ *    need distinct workspaces (and distinct outputs).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising.  `loss` is a device scalar.
+ *  - Argument errors are returned synchronously before anything is enqueued.
+ *  - Ids outside [0, V) are reported on the device: *status_dev is set to
+ *    KD_ERR_BAD_INDEX (if status_dev is not NULL) and the entry contributes
+ *    nothing to the loss or the gradients; p is still normalised over all K
+ *    logits of the row.  NaN or Inf inputs propagate.
+ *  - Results are deterministic: two calls on the same inputs give the same
+ *    bits (fixed-order reductions, no floating-point atomics).
+ */
+#ifndef KD_TOPK_KL_H
+#define KD_TOPK_KL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KD_OK 0
+#define KD_ERR_NULL_ARG 1    /* a required pointer is NULL                      */
+#define KD_ERR_BAD_SHAPE 2   /* T, d, V or K < 1, K > V, K > KD_MAX_K, or V*d,  */
+                             /* chunk*V or T*d exceeds what the kernels address */
+#define KD_ERR_BAD_TAU 3     /* tau <= 0 or not finite                          */
+#define KD_ERR_BAD_CHUNK 4   /* chunk < 1                                       */
+#define KD_ERR_DTYPE 5       /* in_dtype is not KD_BF16 or KD_F32               */
+#define KD_ERR_WORKSPACE 6   /* workspace NULL or smaller than required         */
+#define KD_ERR_BAD_INDEX 7   /* (device) a teacher id is outside [0, V)         */
+#define KD_ERR_HIP 8         /* a HIP launch failed                             */
+
+/* Input element types of `hidden` and `W`. */
+#define KD_BF16 0            /* bfloat16, row-major                             */
+#define KD_F32 1             /* float32, row-major ("fp32 everywhere": the      */
+                             /* gradient chunk is also kept in fp32)            */
+
+/* Largest cache width K accepted (duplicate ids are merged per row in LDS). */
+#define KD_MAX_K 4096
+
+/*
+ * Bytes of device workspace kd_topk_kl_fwd_bwd needs for these sizes; 0 if
+ * the arguments are invalid.  A chunk larger than T is treated as T.  The
+ * size grows as O(chunk*V + V*d) and does not depend on T beyond the chunk
+ * (it holds one chunk's gradient in two layouts, the transposed head and
+ * per-chunk row statistics).
+ */
+size_t kd_topk_kl_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K,
+                                  int64_t chunk, int32_t in_dtype);
+
+/*
+ * Forward and backward of the loss above in one call.
+ *
+ *  hidden        device [T, d] in_dtype, row-major: the student's final hidden
+ *                states (one row per sequence position).
+ *  W             device [V, d] in_dtype, row-major: the output head (lm_head).
+ *  teacher_idx   device [T, K] int32, row-major: cached teacher token ids.
+ *  teacher_logit device [T, K] float32, row-major: their cached logits (any
+ *                per-row offset; only differences matter).
+ *  mask          device [T] uint8, nonzero = the position counts; NULL = all
+ *                positions count.
+ *  tau           temperature > 0 (divides student and teacher logits; the
+ *                loss is multiplied by tau^2).
+ *  chunk         number of sequence rows whose V logits are live at once
+ *                (>= 1; values above T mean T).  The last chunk may be ragged.
+ *  loss          device float32 scalar (written).
+ *  grad_hidden   device [T, d] float32 (overwritten).
+ *  grad_W        device [V, d] float32 (overwritten, accumulated in fp32
+ *                across chunks).
+ *  row_lse       device [T] float32 or NULL: logsumexp_v S[t,:] per row.
+ *  row_kl        device [T] float32 or NULL: KL_t per row (masked rows too).
+ *  workspace     device buffer of at least kd_topk_kl_workspace_bytes(...)
+ *                bytes, 256-byte aligned; its contents on entry do not matter.
+ *  status_dev    device int32 or NULL: set to KD_OK at the start of the
+ *                enqueued work, and to KD_ERR_BAD_INDEX if any id is invalid.
+ *  stream        hipStream_t to enqueue on.
+ *
+ * Returns KD_OK or a host-side error code (nothing is enqueued on error,
+ * except KD_ERR_HIP, after which the outputs are unspecified).
+ */
+int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype,
+                           const int32_t* teacher_idx,
+                           const float* teacher_logit, const uint8_t* mask,
+                           int64_t T, int64_t d, int64_t V, int64_t K,
+                           float tau, int64_t chunk,
+                           float* loss, float* grad_hidden, float* grad_W,
+                           float* row_lse, float* row_kl,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t* status_dev, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kd_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_TOPK_KL_H */

@@ -1,0 +1,85 @@
+"""C ABI: the library loads, exports what the header declares, and rejects bad
+arguments on the host before anything touches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_top_kl_lm_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kd_topk_kl.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kd_\w+)\s*\(", src, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared_functions()) == {"kd_topk_kl_workspace_bytes", "kd_topk_kl_fwd_bwd",
+                                          "kd_status_str"}
+
+
+def test_library_exports_every_declared_symbol():
+    L = kd.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code in range(9):
+        assert kd.status_str(code) and kd.status_str(code) != "unknown status"
+    assert kd.status_str(99) == "unknown status"
+
+
+def test_workspace_bytes_validation_and_scaling():
+    wb = kd.workspace_bytes
+    assert wb(0, 8, 8, 1, 1, 0) == 0
+    assert wb(8, 0, 8, 1, 1, 0) == 0
+    assert wb(8, 8, 8, 9, 1, 0) == 0          # K > V
+    assert wb(8, 8, 8, 1, 0, 0) == 0          # chunk < 1
+    assert wb(8, 8, 8, 1, 1, 7) == 0          # dtype
+    assert wb(8, 8, 5000, 4097, 1, 0) == 0    # K > KD_MAX_K
+    # independent of T beyond the chunk
+    a = wb(32768, 2880, 201088, 100, 4096, 0)
+    b = wb(262144, 2880, 201088, 100, 4096, 0)
+    assert a == b > 0
+    # chunk larger than T is T
+    assert wb(100, 64, 1000, 10, 5000, 0) == wb(100, 64, 1000, 10, 100, 0)
+    # O(chunk*V + V*d): doubling the chunk grows it by about 2 * 2 * chunk * V * 2 bytes
+    c1 = wb(65536, 2880, 201088, 100, 2048, 0)
+    c2 = wb(65536, 2880, 201088, 100, 4096, 0)
+    assert 0.9 < (c2 - c1) / (2 * 2048 * 201216 * 2) < 1.3
+    # fp32 path is larger
+    assert wb(512, 256, 4096, 16, 128, 1) > wb(512, 256, 4096, 16, 128, 0)
+
+
+def _call(**kw):
+    L = kd.lib()
+    args = dict(hidden=0x10000, W=0x20000, dt=0, idx=0x30000, logit=0x40000, mask=None, T=64,
+                d=64, V=1000, K=10, tau=1.0, chunk=32, loss=0x50000, gH=0x60000, gW=0x70000,
+                rl=None, rk=None, ws=0x100000, wsb=1 << 40, status=None, stream=None)
+    args.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kd_topk_kl_fwd_bwd(v(args["hidden"]), v(args["W"]), args["dt"], v(args["idx"]),
+                                v(args["logit"]), v(args["mask"]), args["T"], args["d"], args["V"],
+                                args["K"], args["tau"], args["chunk"], v(args["loss"]), v(args["gH"]),
+                                v(args["gW"]), v(args["rl"]), v(args["rk"]), v(args["ws"]),
+                                args["wsb"], v(args["status"]), v(args["stream"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=None), 1), (dict(W=None), 1), (dict(idx=None), 1), (dict(logit=None), 1),
+    (dict(loss=None), 1), (dict(gH=None), 1), (dict(gW=None), 1),
+    (dict(tau=0.0), 3), (dict(tau=-1.0), 3), (dict(tau=float("nan")), 3), (dict(tau=float("inf")), 3),
+    (dict(T=0), 2), (dict(d=0), 2), (dict(V=0), 2), (dict(K=0), 2), (dict(K=1001), 2),
+    (dict(chunk=0), 4), (dict(chunk=-5), 4), (dict(dt=3), 5),
+    (dict(ws=None), 6), (dict(wsb=1000), 6), (dict(ws=0x100010), 6),
+    (dict(hidden=0x10008), 2),
+])
+def test_host_argument_errors(kw, code):
+    # every case fails in host validation, before any HIP call
+    assert _call(**kw) == code
