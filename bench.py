@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the fused chunked top-K KL loss (forward + backward) on one MI355X.
+
+One step = one call of the whole hot path (count, W^T, and per chunk: forward
+GEMM with the online logsumexp, KL at the teacher ids, recompute GEMM with the
+gradient epilogue, sparse scatter, hidden-gradient GEMM, head-gradient GEMM;
+then the final loss) over one batch of synthetic inputs already resident in
+HBM.  Default workload: T=32768, d=2880, V=201088, K=100, chunk=2048, tau=1,
+bf16 hidden/W (a gpt-oss-20b-sized output head at 32K context).
+
+Prints ONE JSON line.  Extra keys: roofline (dominant kernel, live HIP-event
+timing inside the timed region), cpu_baseline (the fp64 oracle on a bounded
+sample of the same workload, host cores), phases_ms, peak_gib.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec fwd+bwd and % bf16 MFMA peak at d=2880,V=201088,T=32K; peak GiB"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (2.5 PFLOP/s class)
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+GEMM_PHASES = ("gemm_fwd_lse", "gemm_bwd_grad", "gemm_dhidden", "gemm_dW")
+KERNEL_SOURCES = ("chunked_top_kl_lm_amd/csrc/kd_gemm.hpp", "chunked_top_kl_lm_amd/csrc/kd_kernels.hpp",
+                  "chunked_top_kl_lm_amd/csrc/kd_topk_kl.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(x: dict, target_s: float) -> dict:
+    """Time the fp64 oracle (as it stands) on the first rows of the workload."""
+    import numpy as np
+    from oracle import fused_kl
+
+    def run(n):
+        t0 = time.perf_counter()
+        fused_kl(x["hidden"][:n], x["W"], x["teacher_idx"][:n], x["teacher_logit"][:n],
+                 x["mask"][:n], x["tau"], rows_per_block=64)
+        return time.perf_counter() - t0
+
+    n0 = 64
+    t0 = run(n0)
+    n = int(min(max(n0, round(n0 * target_s / max(t0, 1e-3) / 64) * 64), x["hidden"].shape[0]))
+    t = run(n) if n != n0 else t0
+    T, d = x["hidden"].shape
+    V = x["W"].shape[0]
+    return {"value": n / t, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"first {n} of {T} rows, full d={d} V={V}, loss+grads in fp64 "
+                      f"({t:.1f} s; 6*n*d*V = {6 * n * d * V / t / 1e9:.0f} GFLOP/s)",
+            "seconds": t, "rows": n}
+
+
+def load_traffic(kernel: str, per_launch_units: int) -> dict | None:
+    """HBM traffic of the dominant kernel from the committed PMC summary, if it
+    was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except Exception:
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+            "bytes": k["fetch_bytes"] + k["write_bytes"], "scale": rec.get("copy_scale")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1-5 (default 3)")
+    ap.add_argument("--T", type=int, default=None, help="override the sequence length")
+    ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 2 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the fused chunked KL loss runs on a single MI355X "
+              "with no collectives; multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import chunked_top_kl_lm_amd as kd
+    from datagen import config_for, make_inputs
+    from tests.gpu_util import to_device
+
+    over = {}
+    if args.T:
+        over["T"] = args.T
+    cfg = config_for(args.workload, **over)
+    chunk = args.chunk or cfg.chunk
+    t_gen = time.perf_counter()
+    x = make_inputs(cfg, seed=args.seed, topk_backend="torch-cuda")
+    t_gen = time.perf_counter() - t_gen
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    dev = torch.device("cuda:0")
+    t = to_device(x)
+    T, d = t["hidden"].shape
+    V = t["W"].shape[0]
+    K = t["teacher_idx"].shape[1]
+    dt = kd.KD_BF16 if x["dtype"] == "bf16" else kd.KD_F32
+    ws = torch.empty(kd.workspace_bytes(T, d, V, K, chunk, dt), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = (torch.empty((), dtype=torch.float32, device=dev), torch.empty((T, d), dtype=torch.float32, device=dev),
+           torch.empty((V, d), dtype=torch.float32, device=dev))
+    eff_chunk = min(chunk, T)
+    nchunks = -(-T // eff_chunk)
+    nslots = kd.KD_NUM_PHASES * nchunks + 2
+
+    def call(events=None):
+        kd.fwd_bwd(t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"], tau=x["tau"],
+                   chunk=chunk, workspace=ws, status=status, out=out, events=events)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # per-step event sets (created by recording once)
+    ev_sets = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nslots)]
+        for e in evs:
+            e.record()
+        ev_sets.append(evs)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        call(ev_sets[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+    peak_gib = torch.cuda.max_memory_allocated() / 2**30
+
+    # phase times per call
+    phase_ms = {p: 0.0 for p in kd.PHASES}
+    pro = fin = 0.0
+    for evs in ev_sets:
+        for c in range(nchunks):
+            for p, name in enumerate(kd.PHASES):
+                i = c * kd.KD_NUM_PHASES + p
+                phase_ms[name] += evs[2 * i].elapsed_time(evs[2 * i + 1])
+        i = kd.KD_NUM_PHASES * nchunks
+        pro += evs[2 * i].elapsed_time(evs[2 * i + 1])
+        fin += evs[2 * i + 2].elapsed_time(evs[2 * i + 3])
+    phase_ms = {k: v / args.steps for k, v in phase_ms.items()}
+    phase_ms["prologue"] = pro / args.steps
+    phase_ms["finalize"] = fin / args.steps
+
+    flops = 8.0 * T * d * V
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if dt == kd.KD_BF16 else PEAK_F32_TFLOPS
+    dom = max(GEMM_PHASES, key=lambda k: phase_ms[k])
+    launch_ms = phase_ms[dom] / nchunks
+    # algorithmic work per launch: 2*d*V FLOPs per token, R = chunk tokens per launch
+    # (average over launches; the last chunk may be ragged)
+    alg_flops = 2.0 * d * V * T / nchunks
+    achieved = alg_flops / (launch_ms * 1e-3) / 1e12
+    traffic = load_traffic(dom, eff_chunk)
+
+    if args.copy_probe:
+        src = torch.empty(2**30 // 2, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x["dtype"],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: lm_head KL distillation T={T} d={d} V={V} K={K} "
+                               f"chunk={chunk} tau={x['tau']}",
+                   "T": T, "d": d, "V": V, "K": K, "chunk": chunk, "tau": x["tau"],
+                   "global_batch": 1, "seq_len": T, "parallelism": "single-gpu"},
+        "tflops": tflops,
+        "pct_mfma_peak": 100.0 * tflops / peak,
+        "peak_gib": peak_gib,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "launch_ms": launch_ms,
+                     "alg_flops_per_launch": alg_flops,
+                     "traffic": traffic},
+        "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "wall_s_timed": wall,
+        "input_gen_s": t_gen,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        del t, ws, out
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

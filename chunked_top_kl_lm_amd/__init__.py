@@ -10,11 +10,14 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["KD_BF16", "KD_F32", "KdError", "lib", "workspace_bytes", "fwd_bwd",
+__all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
            "status_str", "STATUS"]
 
 KD_BF16 = 0
 KD_F32 = 1
+KD_NUM_PHASES = 8
+PHASES = ("pad_transpose_h", "gemm_fwd_lse", "kl_rows", "gemm_bwd_grad", "scatter_sparse",
+          "gemm_dhidden", "dhidden_reduce", "gemm_dW")
 STATUS = {0: "KD_OK", 1: "KD_ERR_NULL_ARG", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_TAU",
           4: "KD_ERR_BAD_CHUNK", 5: "KD_ERR_DTYPE", 6: "KD_ERR_WORKSPACE",
           7: "KD_ERR_BAD_INDEX", 8: "KD_ERR_HIP"}
@@ -43,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.kd_topk_kl_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, i64,
                                          vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.kd_topk_kl_fwd_bwd.restype = i32
+        L.kd_topk_kl_fwd_bwd_timed.argtypes = L.kd_topk_kl_fwd_bwd.argtypes + [vp]
+        L.kd_topk_kl_fwd_bwd_timed.restype = i32
         L.kd_status_str.argtypes = [i32]
         L.kd_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -63,7 +68,7 @@ def _ptr(t):
 
 def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
             chunk: int = 2048, row_stats: bool = False, workspace=None, status=None,
-            out=None):
+            out=None, events=None):
     """Loss and gradients of the top-K KL distillation loss on the GPU.
 
     hidden [T,d] and W [V,d]: torch bfloat16 or float32 CUDA tensors
@@ -73,7 +78,9 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     also (row_lse [T], row_kl [T]).  `out` may hold preallocated
     (loss, grad_hidden, grad_W[, row_lse, row_kl]); `workspace` a uint8 CUDA
     tensor of at least workspace_bytes(...) bytes; `status` an int32 CUDA
-    tensor of one element that receives the device status.
+    tensor of one element that receives the device status.  `events`, for
+    measurement only, is a sequence of 2 * (KD_NUM_PHASES * nchunks + 2)
+    already-recorded torch.cuda.Event objects (see kd_topk_kl_fwd_bwd_timed).
     """
     import torch
     L = lib()
@@ -110,10 +117,15 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = L.kd_topk_kl_fwd_bwd(_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit),
-                              _ptr(mask), T, d, V, K, float(tau), int(chunk), _ptr(loss), _ptr(gH),
-                              _ptr(gW), _ptr(rl), _ptr(rk), _ptr(workspace), workspace.numel(),
-                              _ptr(status), ctypes.c_void_p(stream))
+    args = (_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit),
+            _ptr(mask), T, d, V, K, float(tau), int(chunk), _ptr(loss), _ptr(gH),
+            _ptr(gW), _ptr(rl), _ptr(rk), _ptr(workspace), workspace.numel(),
+            _ptr(status), ctypes.c_void_p(stream))
+    if events is None:
+        rc = L.kd_topk_kl_fwd_bwd(*args)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        rc = L.kd_topk_kl_fwd_bwd_timed(*args, arr)
     if rc != 0:
         raise KdError(rc)
     if row_stats:

@@ -124,8 +124,13 @@ GemmShape make_shape(const void* A, int64_t lda, int M, const void* B, int64_t l
 template <class E>
 int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx, const float* logit,
             const uint8_t* mask, float tau, float* loss, float* grad_hidden, float* grad_W, float* row_lse,
-            float* row_kl, char* ws, int32_t* status, hipStream_t st) {
+            float* row_kl, char* ws, int32_t* status, hipStream_t st, void* const* events) {
   typedef typename E::T T;
+  // timing markers (measurement entry point only)
+  auto mark = [&](int64_t slot, int end) {
+    if (events) hipEventRecord((hipEvent_t)events[2 * slot + end], st);
+  };
+  const int64_t pro_slot = (int64_t)KD_NUM_PHASES * P.nchunks;
   int* count = (int*)(ws + P.off_scalar);
   double* loss_acc = (double*)(ws + P.off_scalar + 8);
   T* Wt = (T*)(ws + P.off_wt);
@@ -142,6 +147,7 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
   const int64_t T_ = P.T, d = P.d, V = P.V, K = P.K;
   const float c2 = kLog2e / tau;
 
+  mark(pro_slot, 0);
   hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, st, mask, T_, count, loss_acc, status);
   KD_LAUNCH_CHECK();
   // W^T, zero-padded to [d_p][V_p]
@@ -159,11 +165,14 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     ldw = P.d_p;
   }
   const int64_t kbytes_d = P.d_p * P.eb;
+  mark(pro_slot, 1);
 
   for (int64_t c = 0; c < P.nchunks; ++c) {
     const int64_t c0 = c * P.chunk;
     const int R = (int)std::min<int64_t>(P.chunk, T_ - c0);
     const int64_t Rt = round_up(R, kBN);     // rows covered by the GEMM tiles this chunk
+    const int64_t slot = c * KD_NUM_PHASES;
+    mark(slot + 0, 0);
     const T* Hc = (const T*)hidden + c0 * d;
     const T* Hsrc = Hc;
     int64_t ldh = d;
@@ -179,51 +188,68 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.R_p / 64), (unsigned)(P.d_p / 64)), dim3(256), 0,
                        st, Hc, d, (int64_t)R, d, Ht, P.R_p);
     KD_LAUNCH_CHECK();
+    mark(slot + 0, 1);
 
     const uint8_t* mask_c = mask ? mask + c0 : nullptr;
     const int32_t* idx_c = idx + c0 * K;
     const float* logit_c = logit + c0 * K;
 
     // forward: z^T = W H_c^T -> LSE partials
+    mark(slot + 1, 0);
     {
       GemmShape g = make_shape(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
       EpiLsePartial epi{part, (int)P.R_p, (int)V, c2};
       if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
+    mark(slot + 1, 1);
+    mark(slot + 2, 0);
     hipLaunchKernelGGL(kl_rows_kernel<E>, dim3(R), dim3(256), 0, st, (const float2*)part, (int)P.R_p, (int)P.nvt,
                        Hsrc, ldh, Wsrc, ldw, (int)(P.d_p * P.eb / 16), idx_c, logit_c, (int)K, (int)V, tau, lse2,
                        rowkl, row_lse ? row_lse + c0 : nullptr, row_kl ? row_kl + c0 : nullptr, status);
     KD_LAUNCH_CHECK();
     hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(256), 0, st, (const double*)rowkl, mask_c, R, loss_acc);
     KD_LAUNCH_CHECK();
+    mark(slot + 2, 1);
+    mark(slot + 3, 0);
     // backward recompute: G = (tau/N) m q, both layouts
     {
       GemmShape g = make_shape(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
       EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse2, mask_c, count, tau, c2, (int)V, R};
       if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
+    mark(slot + 3, 1);
+    mark(slot + 4, 0);
     hipLaunchKernelGGL(scatter_sparse_kernel<E>, dim3(R), dim3(128), 0, st, idx_c, logit_c, mask_c, (int)K, (int)V,
                        tau, (const int*)count, G, P.V_p, Gt, P.R_p);
     KD_LAUNCH_CHECK();
+    mark(slot + 4, 1);
+    mark(slot + 5, 0);
     // dH_c = G W  (A = G [Rt x V_p], B = W^T [d x V_p]), split-K over V
     {
       GemmShape g = make_shape(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits);
       EpiStoreSplit epi{dhp, P.Nd_p, P.R_p * P.Nd_p};
       if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      mark(slot + 5, 1);
+      mark(slot + 6, 0);
       const int64_t n = (int64_t)R * d;
       hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
                          (const float*)dhp, P.Nd_p, P.R_p * P.Nd_p, P.splits, R, (int)d, grad_hidden + c0 * d, d);
       KD_LAUNCH_CHECK();
+      mark(slot + 6, 1);
     }
+    mark(slot + 7, 0);
     // dW (+)= G^T H_c  (A = G^T [V_p x R_p], B = H_c^T [d x R_p])
     {
       GemmShape g = make_shape(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1);
       EpiAccum epi{grad_W, d, (int)V, (int)d, c == 0 ? 1 : 0};
       if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
+    mark(slot + 7, 1);
   }
+  mark(pro_slot + 1, 0);
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, st, (const double*)loss_acc, (const int*)count, tau, loss);
   KD_LAUNCH_CHECK();
+  mark(pro_slot + 1, 1);
   return KD_OK;
 }
 
@@ -238,11 +264,11 @@ size_t kd_topk_kl_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K, in
   return p.total;
 }
 
-int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
-                           const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
-                           int64_t K, float tau, int64_t chunk, float* loss, float* grad_hidden, float* grad_W,
-                           float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,
-                           int32_t* status_dev, void* stream) {
+static int32_t fwd_bwd_impl(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                            const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
+                            int64_t K, float tau, int64_t chunk, float* loss, float* grad_hidden, float* grad_W,
+                            float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,
+                            int32_t* status_dev, void* stream, void* const* events) {
   if (!hidden || !W || !teacher_idx || !teacher_logit || !loss || !grad_hidden || !grad_W) return KD_ERR_NULL_ARG;
   if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_BAD_TAU;
   kd::Plan p;
@@ -253,9 +279,28 @@ int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype, 
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == KD_BF16)
     return kd::run<kd::Bf16>(p, hidden, W, teacher_idx, teacher_logit, mask, tau, loss, grad_hidden, grad_W, row_lse,
-                             row_kl, (char*)workspace, status_dev, s);
+                             row_kl, (char*)workspace, status_dev, s, events);
   return kd::run<kd::F32>(p, hidden, W, teacher_idx, teacher_logit, mask, tau, loss, grad_hidden, grad_W, row_lse,
-                          row_kl, (char*)workspace, status_dev, s);
+                          row_kl, (char*)workspace, status_dev, s, events);
+}
+
+int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                           const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
+                           int64_t K, float tau, int64_t chunk, float* loss, float* grad_hidden, float* grad_W,
+                           float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,
+                           int32_t* status_dev, void* stream) {
+  return fwd_bwd_impl(hidden, W, in_dtype, teacher_idx, teacher_logit, mask, T, d, V, K, tau, chunk, loss,
+                      grad_hidden, grad_W, row_lse, row_kl, workspace, workspace_bytes, status_dev, stream, nullptr);
+}
+
+int32_t kd_topk_kl_fwd_bwd_timed(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                                 const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
+                                 int64_t K, float tau, int64_t chunk, float* loss, float* grad_hidden, float* grad_W,
+                                 float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,
+                                 int32_t* status_dev, void* stream, void* const* events) {
+  if (!events) return KD_ERR_NULL_ARG;
+  return fwd_bwd_impl(hidden, W, in_dtype, teacher_idx, teacher_logit, mask, T, d, V, K, tau, chunk, loss,
+                      grad_hidden, grad_W, row_lse, row_kl, workspace, workspace_bytes, status_dev, stream, events);
 }
 
 const char* kd_status_str(int32_t s) {

@@ -118,6 +118,35 @@ int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype,
                            void* workspace, size_t workspace_bytes,
                            int32_t* status_dev, void* stream);
 
+/* Number of timed phases per chunk (see kd_topk_kl_fwd_bwd_timed). */
+#define KD_NUM_PHASES 8
+
+/*
+ * kd_topk_kl_fwd_bwd with timing markers, for measurement.  `events` points
+ * to 2 * (KD_NUM_PHASES * nchunks + 2) hipEvent_t created by the caller,
+ * nchunks = ceil(T / min(chunk, T)).  The call records events[2*i] before and
+ * events[2*i + 1] after the launches of
+ *   i = c * KD_NUM_PHASES + p   phase p of chunk c:
+ *       0 zero-padded H_c and H_c^T, 1 forward GEMM with the logsumexp
+ *       partials, 2 KL rows and the chunk's loss sum, 3 recompute GEMM with
+ *       the gradient epilogue, 4 sparse teacher scatter, 5 hidden-gradient
+ *       GEMM, 6 its split-K reduction, 7 head-gradient GEMM;
+ *   i = KD_NUM_PHASES * nchunks      the prologue (count N, W^T);
+ *   i = KD_NUM_PHASES * nchunks + 1  the final loss.
+ * Everything else is as for kd_topk_kl_fwd_bwd; KD_ERR_NULL_ARG if events is
+ * NULL.
+ */
+int32_t kd_topk_kl_fwd_bwd_timed(const void* hidden, const void* W, int32_t in_dtype,
+                                 const int32_t* teacher_idx,
+                                 const float* teacher_logit, const uint8_t* mask,
+                                 int64_t T, int64_t d, int64_t V, int64_t K,
+                                 float tau, int64_t chunk,
+                                 float* loss, float* grad_hidden, float* grad_W,
+                                 float* row_lse, float* row_kl,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t* status_dev, void* stream,
+                                 void* const* events);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kd_status_str(int32_t status);
 

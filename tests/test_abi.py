@@ -20,7 +20,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {"kd_topk_kl_workspace_bytes", "kd_topk_kl_fwd_bwd",
-                                          "kd_status_str"}
+                                          "kd_topk_kl_fwd_bwd_timed", "kd_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -83,3 +83,12 @@ def _call(**kw):
 def test_host_argument_errors(kw, code):
     # every case fails in host validation, before any HIP call
     assert _call(**kw) == code
+
+
+def test_timed_entry_requires_events():
+    L = kd.lib()
+    v = ctypes.c_void_p
+    rc = L.kd_topk_kl_fwd_bwd_timed(v(0x10000), v(0x20000), 0, v(0x30000), v(0x40000), None, 64, 64,
+                                    1000, 10, 1.0, 32, v(0x50000), v(0x60000), v(0x70000), None, None,
+                                    v(0x100000), 1 << 40, None, None, None)
+    assert rc == 1
