@@ -10,16 +10,15 @@
 // of the traffic and let a single LDS layout and MFMA schedule serve all.
 //
 // Tiling.  A block computes a BM x BN tile with 64 * WM * WN threads; each
-// wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles.  K is
-// consumed in steps of 128 bytes per row (64 bf16 or 32 fp32).  Tiles are
-// staged through LDS, double-buffered, with a 16-byte XOR swizzle (unit u of
-// row r is stored at unit u ^ (r & 7)) so that both the 16-byte global->LDS
-// writes and the 16-byte fragment reads are bank-conflict free.
+// wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32x16 (bf16) or 32x32x2
+// (fp32) MFMA tiles.  K is consumed in stages of 64 bytes per row (32 bf16 or
+// 16 fp32), moved global -> LDS by direct LDS-DMA loads into a ring of STAGES
+// buffers (see gemm_nt_kernel).
 //
 // Bounds.  Operand rows past the matrix end are read through buffer
 // resources whose size ends at the last valid row, so the hardware returns
 // zeros for them; the K extent of every operand is padded with zeros to a
-// multiple of 128 bytes by the caller.
+// multiple of 64 bytes by the caller.
 //
 // The MFMA accumulator layout (32x32 tiles): register r of lane l holds
 // C[8*(r/4) + 4*(l/32) + r%4][l%32].  So each lane holds one column n and a
@@ -121,23 +120,105 @@ struct EpiCtx {
   char* smem;
 };
 
-template <class E, int BM, int BN, int WM, int WN>
-struct GemmCfg {
+// ---------------------------------------------------------------------------
+// LDS staging.  Each stage holds A [BM rows x 64 B] then B [BN rows x 64 B].  A wave's
+// LDS-DMA instruction writes 1 KB of consecutive LDS (lane l -> bytes
+// 16l..16l+15), i.e. 16 rows of 64 B; the swizzle is applied on the global
+// side: the lane that fills slot s of row r fetches logical 16-byte unit
+// s ^ f(r), f(r) = (r >> 2) & 3.  gfx950 serves a 128-bit LDS read in 4
+// cycles when conflict-free (256 B/clk); with this f the MFMA fragment reads
+// (32 consecutive rows, two units per row) measure conflict-free with the
+// SQ_LDS_BANK_CONFLICT counter, whereas f = ((r>>1)^(r>>3)) & 3 and the
+// 128-byte-row layout with f = r & 7 measure 2-way conflicts.
+//
+// Ordering: the loads for stage `it` are waited for with s_waitcnt vmcnt
+// (counting only this wave's later-issued loads), then a workgroup barrier
+// makes every wave's LDS writes visible; the stage overwritten next is the
+// one all waves finished reading before that same barrier.
+// ---------------------------------------------------------------------------
+// 16-byte slot permutation of a 64-byte LDS row r (see above).
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <class E, int BM, int BN, int WM, int WN, int STAGES>
+struct PipeCfg {
   static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int kLdsStage = (BM + BN) * 128;
-  static constexpr int kLds = 2 * kLdsStage;
-  static constexpr int UA = BM * 8 / kThreads;   // 16-byte units of A per thread per stage
-  static constexpr int UB = BN * 8 / kThreads;
+  static constexpr int RB = 64;
+  static constexpr int kStage = (BM + BN) * RB;
+  static constexpr int kLds = STAGES * kStage;
+  static constexpr int IA = BM / 16 / NW;     // DMA instructions per wave per stage (A)
+  static constexpr int IB = BN / 16 / NW;
+  static constexpr int kPer = IA + IB;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert((BM * 8) % kThreads == 0 && (BN * 8) % kThreads == 0, "loader split");
+  static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "DMA split");
+  static_assert(STAGES >= 2 && (STAGES - 1) * (IA + IB) < 64, "vmcnt range");
 };
 
-template <class E, int BM, int BN, int WM, int WN, class Epi>
+template <class C, int BM>
+__device__ __forceinline__ void dma_stage(char* s, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          const uint32_t* voffA, const uint32_t* voffB, int wid, uint32_t ko) {
+#pragma unroll
+  for (int i = 0; i < C::IA; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(s + (wid + C::NW * i) * 1024),
+                                             16, voffA[i] + ko, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::IB; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (__attribute__((address_space(3))) void*)(s + BM * C::RB + (wid + C::NW * i) * 1024), 16, voffB[i] + ko, 0,
+        0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Main loop.  The per-stage barrier sits in the middle of a stage, so that
+// the MFMA pipe never drains on it:
+//
+//   iteration it (fa0/fb0 already hold K-group 0 of stage it; a K-group is
+//   32 bytes of K, one 16-byte unit per half-wave):
+//     read K-group 1 fragments of stage it        } interleaved with the
+//     MFMAs of K-group 0                          } MFMAs
+//     wait for this wave's ds_reads and for stage it+1's DMA; barrier
+//     DMA of stage it+STAGES into the buffer of stage it (all waves are
+//     done reading it), read K-group 0 of stage it+1, MFMAs of K-group 1
+//
+// The DMA and ds_read issues are spread between MFMAs with
+// sched_group_barrier so the two waves of a SIMD keep its MFMA pipe fed.
+// ---------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ void read_frags(const char* s, uint32_t aRow0, uint32_t bRow0, uint32_t uoff,
+                                           u32x4 (&fa)[C::FM], u32x4 (&fb)[C::FN]) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) fa[i] = *(const u32x4*)(s + aRow0 + i * 32 * C::RB + uoff);
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) fb[j] = *(const u32x4*)(s + bRow0 + j * 32 * C::RB + uoff);
+}
+
+template <class E, class C>
+__device__ __forceinline__ void mfma_all(f32x16 (&acc)[C::FM][C::FN], const u32x4 (&fa)[C::FM],
+                                         const u32x4 (&fb)[C::FN]) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) mfma_group<E>(acc[i][j], fa[i], fb[j]);
+}
+
+template <class E, int BM, int BN, int WM, int WN, int STAGES, class Epi>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi epi) {
-  typedef GemmCfg<E, BM, BN, WM, WN> C;
-  __shared__ __attribute__((aligned(16))) char smem[C::kLds];
+  typedef PipeCfg<E, BM, BN, WM, WN, STAGES> C;
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
 
   const TilePos pos = tile_position(g);
   if (!pos.valid) return;
@@ -155,26 +236,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
   const int rowsA = min(BM, g.M - pos.tm * BM);
   const int rowsB = min(BN, g.N - pos.tn * BN);
   const int64_t strideA = g.lda * E::kBytes, strideB = g.ldb * E::kBytes;
-  const char* baseA = (const char*)g.A + (int64_t)pos.tm * BM * strideA + (int64_t)kt0 * 128;
-  const char* baseB = (const char*)g.B + (int64_t)pos.tn * BN * strideB + (int64_t)kt0 * 128;
-  // rowsA may be <= 0 only for an empty matrix, which the host never launches.
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(baseA, (uint32_t)(rowsA * strideA - kt0 * 128));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(baseB, (uint32_t)(rowsB * strideB - kt0 * 128));
+  const char* baseA = (const char*)g.A + (int64_t)pos.tm * BM * strideA + (int64_t)kt0 * C::RB;
+  const char* baseB = (const char*)g.B + (int64_t)pos.tn * BN * strideB + (int64_t)kt0 * C::RB;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(baseA, (uint32_t)(rowsA * strideA - kt0 * C::RB));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(baseB, (uint32_t)(rowsB * strideB - kt0 * C::RB));
 
-  // Loader: unit q = tid + kThreads * i covers row q >> 3, 16-byte unit q & 7.
-  uint32_t goffA[C::UA], goffB[C::UB];
-  uint32_t loffA[C::UA], loffB[C::UB];
+  uint32_t voffA[C::IA], voffB[C::IB];
 #pragma unroll
-  for (int i = 0; i < C::UA; ++i) {
-    const int q = tid + C::kThreads * i, r = q >> 3, u = q & 7;
-    goffA[i] = (uint32_t)(r * strideA + u * 16);
-    loffA[i] = (uint32_t)(r * 128 + ((u ^ (r & 7)) << 4));
+  for (int i = 0; i < C::IA; ++i) {
+    const int r = 16 * (wid + C::NW * i) + (lane >> 2);
+    voffA[i] = (uint32_t)(r * strideA + (((lane & 3) ^ swz64(r)) << 4));
   }
 #pragma unroll
-  for (int i = 0; i < C::UB; ++i) {
-    const int q = tid + C::kThreads * i, r = q >> 3, u = q & 7;
-    goffB[i] = (uint32_t)(r * strideB + u * 16);
-    loffB[i] = (uint32_t)(BM * 128 + r * 128 + ((u ^ (r & 7)) << 4));
+  for (int i = 0; i < C::IB; ++i) {
+    const int r = 16 * (wid + C::NW * i) + (lane >> 2);
+    voffB[i] = (uint32_t)(r * strideB + (((lane & 3) ^ swz64(r)) << 4));
   }
 
   f32x16 acc[C::FM][C::FN];
@@ -185,53 +261,61 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 sa[C::UA], sb[C::UB];
-  auto gload = [&](int kt) {
-    const uint32_t ko = (uint32_t)kt * 128u;
-#pragma unroll
-    for (int i = 0; i < C::UA; ++i) sa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, goffA[i] + ko, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::UB; ++i) sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, goffB[i] + ko, 0, 0);
-  };
-  auto lstore = [&](int stage) {
-    char* s = smem + stage * C::kLdsStage;
-#pragma unroll
-    for (int i = 0; i < C::UA; ++i) *(u32x4*)(s + loffA[i]) = sa[i];
-#pragma unroll
-    for (int i = 0; i < C::UB; ++i) *(u32x4*)(s + loffB[i]) = sb[i];
-  };
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int fsw = swz64(wm * C::TM + frow);
+  const uint32_t aRow0 = (uint32_t)((wm * C::TM + frow) * C::RB);
+  const uint32_t bRow0 = (uint32_t)(BM * C::RB + (wn * C::TN + frow) * C::RB);
+  const uint32_t uoff0 = (uint32_t)(((0 + fhalf) ^ fsw) << 4);
+  const uint32_t uoff1 = (uint32_t)(((2 + fhalf) ^ fsw) << 4);
 
-  // Fragment read offsets: row (lane & 31) of each 32-row MFMA tile, unit
-  // 2*grp + (lane >> 5), swizzled by (row & 7) == (lane & 7).
-  const int frow = lane & 31, fhalf = lane >> 5, fsw = lane & 7;
-  const uint32_t aRow0 = (uint32_t)((wm * C::TM + frow) * 128);
-  const uint32_t bRow0 = (uint32_t)(BM * 128 + (wn * C::TN + frow) * 128);
+  // Stages past the end of K are still issued, at an offset beyond the
+  // buffer range: the hardware returns zeros without a memory access.  Every
+  // iteration thus issues exactly one stage and the vmcnt bookkeeping is the
+  // same constant in all of them.
+  auto kofs = [&](int kt) -> uint32_t { return kt < nk ? (uint32_t)kt * C::RB : 0x80000000u; };
 
+  u32x4 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
   if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) gload(it + 1);
-    const char* s = smem + cur * C::kLdsStage;
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const uint32_t uoff = (uint32_t)((((2 * grp + fhalf) ^ fsw)) << 4);
-      u32x4 fa[C::FM], fb[C::FN];
+    for (int st = 0; st < STAGES; ++st) dma_stage<C, BM>(smem + st * C::kStage, ra, rb, voffA, voffB, wid, kofs(st));
+    wait_vmcnt<(STAGES - 1) * C::kPer>();                  // stage 0 has landed
+    lds_barrier();
+    read_frags<C>(smem, aRow0, bRow0, uoff0, fa0, fb0);
+
+    for (int it = 0; it < nk - 1; ++it) {
+      const char* s = smem + (it % STAGES) * C::kStage;
+      read_frags<C>(s, aRow0, bRow0, uoff1, fa1, fb1);
+      mfma_all<E, C>(acc, fa0, fb0);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) fa[i] = *(const u32x4*)(s + aRow0 + i * 32 * 128 + uoff);
+      for (int q = 0; q < C::FM + C::FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+      }
+      // this wave's reads of stage `it` have returned; stage it+1 has landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+      wait_vmcnt<(STAGES - 2) * C::kPer>();
+      lds_barrier();
+      dma_stage<C, BM>(smem + (it % STAGES) * C::kStage, ra, rb, voffA, voffB, wid, kofs(it + STAGES));
+      read_frags<C>(smem + ((it + 1) % STAGES) * C::kStage, aRow0, bRow0, uoff0, fa0, fb0);
+      mfma_all<E, C>(acc, fa1, fb1);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) fb[j] = *(const u32x4*)(s + bRow0 + j * 32 * 128 + uoff);
+      for (int q = 0; q < C::kPer; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 VMEM (DMA)
+      }
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) mfma_group<E>(acc[i][j], fa[i], fb[j]);
+      for (int q = 0; q < C::FM + C::FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
     }
-    if (it + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+    // last stage
+    read_frags<C>(smem + ((nk - 1) % STAGES) * C::kStage, aRow0, bRow0, uoff1, fa1, fb1);
+    mfma_all<E, C>(acc, fa0, fb0);
+    mfma_all<E, C>(acc, fa1, fb1);
+    wait_vmcnt<0>();                                       // drain the tail loads before LDS is reused
   }
+  lds_barrier();
 
   EpiCtx ctx;
   ctx.m0 = pos.tm * BM + wm * C::TM;

@@ -31,9 +31,14 @@
 namespace kd {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
+// GEMM tile configuration shared by the four contractions: 256 x 256 block
+// tiles, 8 waves as 2 (M) x 4 (N), each wave 128 x 64; 3 LDS stages of 64
+// bytes of K (96 KB of LDS).
+constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4, kStages = 3;
 constexpr int kWaveM = kBM / kWM;     // vocabulary strip of one LSE partial
 constexpr int kThreads = 64 * kWM * kWN;
+constexpr int kKStep = 64;            // bytes of K per pipeline stage
+constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -71,13 +76,23 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
     return KD_ERR_BAD_SHAPE;
   if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_p * P.eb >= (1ll << 32))
     return KD_ERR_BAD_SHAPE;
-  // split-K of the hidden-gradient GEMM: aim for ~4 tiles in flight per CU
+  // split-K of the hidden-gradient GEMM (output only chunk x d): pick the
+  // split count whose grid fills whole waves of 256 CUs best, with at least
+  // two waves when the K extent allows, and a small penalty per split for
+  // the partial-sum traffic.
   const int64_t tiles = cdiv(P.R_p, kBM) * cdiv(P.Nd_p, kBN);
-  const int64_t k_tiles = P.V_p * P.eb / 128;
-  int64_t s = cdiv(1024, tiles);
-  if (s > k_tiles) s = k_tiles;
-  if (s < 1) s = 1;
-  P.splits = (int)s;
+  const int64_t k_tiles = P.V_p * P.eb / kKStep;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= 64 && sp <= k_tiles; ++sp) {
+    const int64_t blocks = tiles * sp;
+    const double waves = (double)blocks / kNumCU;
+    double cost = (double)cdiv(blocks, kNumCU) / waves + 0.004 * sp;
+    if (blocks < 2 * kNumCU) cost += 1.0;                  // too little parallelism
+    if (k_tiles / sp < 16) cost += 1.0;                     // splits too thin
+    if (cost < best_cost) { best_cost = cost; best = sp; }
+  }
+  P.splits = best;
 
   const size_t e = (size_t)P.eb;
   size_t o = 0;
@@ -100,7 +115,8 @@ template <class E, class Epi>
 hipError_t launch_gemm(const GemmShape& g, const Epi& epi, hipStream_t st) {
   const int nb = g.tiles_m * g.tiles_n * g.splits;
   const int grid = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_nt_kernel<E, kBM, kBN, kWM, kWN, Epi>), dim3(grid), dim3(kThreads), 0, st, g, epi);
+  hipLaunchKernelGGL((gemm_nt_kernel<E, kBM, kBN, kWM, kWN, kStages, Epi>), dim3(grid), dim3(kThreads), 0, st, g,
+                     epi);
   return hipGetLastError();
 }
 
@@ -108,7 +124,7 @@ GemmShape make_shape(const void* A, int64_t lda, int M, const void* B, int64_t l
                      int splits) {
   GemmShape g;
   g.A = A; g.B = B; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N;
-  g.k_tiles = (int)(k_bytes / 128);
+  g.k_tiles = (int)(k_bytes / kKStep);
   g.splits = splits;
   g.k_tiles_per_split = (int)cdiv(g.k_tiles, splits);
   g.tiles_m = (int)cdiv(M, kBM);
