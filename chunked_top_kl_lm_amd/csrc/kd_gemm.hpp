@@ -117,7 +117,7 @@ struct EpiCtx {
   int split;
   int tm, tn;
   int wm, wn;
-  char* smem;
+  char* smem;   // the LDS ring (free once the main loop has ended)
 };
 
 // ---------------------------------------------------------------------------
@@ -215,6 +215,10 @@ __device__ __forceinline__ void mfma_all(f32x16 (&acc)[C::FM][C::FN], const u32x
     for (int j = 0; j < C::FN; ++j) mfma_group<E>(acc[i][j], fa[i], fb[j]);
 }
 
+// One block per output tile (grid = all tiles, rounded up to a multiple of
+// 8): the dispatcher hands a CU its next tile as soon as the previous one
+// ends.  Used where the epilogue is light; gemm_nt_kernel (persistent) is
+// used where the epilogue has to overlap with the next tile's loads.
 template <class E, int BM, int BN, int WM, int WN, int STAGES, class Epi>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi epi) {
   typedef PipeCfg<E, BM, BN, WM, WN, STAGES> C;

@@ -21,6 +21,23 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // GEMM epilogues
 // ---------------------------------------------------------------------------
 
+// Rows of a wave's strip at or past `rows_valid` (vocabulary padding, whose
+// logits are exactly 0 because their A rows read as zeros) are pushed to
+// about -1e38 so that they vanish from maxima and from sums of exp2.  The
+// clamp is arithmetic (no per-element predicate), so it costs a few VALU
+// operations per element on every tile and keeps no lane masks alive.
+template <int FM, int FN>
+__device__ __forceinline__ void clamp_padding_rows(f32x16 (&acc)[FM][FN], int rows_valid, int lane) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float lim = ((float)(rows_valid - 32 * i - acc_row(r, lane)) - 0.5f) * 1e38f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j][r] = fminf(acc[i][j][r], lim);
+    }
+}
+
 // Forward pass of a chunk: per (vocabulary strip of one wave, row t) the
 // running max and sum of exp2 -- the partial logsumexp that the online merge
 // folds into the row's full-vocabulary normaliser.  The logits themselves are
@@ -36,28 +53,27 @@ struct EpiLsePartial {
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
     const int vt = c.m0 / (FM * 32);
-    const bool full = c.m0 + FM * 32 <= V;
+    const int rows_valid = V - c.m0;          // vocabulary rows of this strip that exist
+    if (rows_valid <= 0) {                    // strip entirely in the padding
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (c.lane < 32) part[(int64_t)vt * ldp + c.n0 + 32 * j + c.lane] = make_float2(-INFINITY, 0.f);
+      return;
+    }
+    clamp_padding_rows<FM, FN>(acc, rows_valid, c.lane);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = c.m0 + 32 * i + acc_row(r, c.lane);
-          if (full || v < V) mx = fmaxf(mx, acc[i][j][r] * c2);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;   // c2 > 0: max commutes with the scaling
       float sm = 0.f;
-      if (mx != -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = c.m0 + 32 * i + acc_row(r, c.lane);
-            if (full || v < V) sm += fast_exp2(acc[i][j][r] * c2 - mx);
-          }
-      }
+        for (int r = 0; r < 16; ++r) sm += fast_exp2(acc[i][j][r] * c2 - mx);
       sm += __shfl_xor(sm, 32);
       if (c.lane < 32) part[(int64_t)vt * ldp + c.n0 + 32 * j + c.lane] = make_float2(mx, sm);
     }
@@ -66,7 +82,7 @@ struct EpiLsePartial {
 
 // Backward recompute of a chunk: the logit gradient of the loss,
 // G[t,v] = (tau/N) m_t q[t,v], written in two layouts (G [R_p][V_p] and
-// G^T [V_p][R_p]) for the two gradient GEMMs.  The sparse teacher part
+// G^T [V_p][R_p]) for the two gradient GEMMs; entries at v >= V are unused.  The sparse teacher part
 // -(tau/N) m_t P[t,v] is subtracted afterwards by scatter_sparse_kernel.
 template <class E>
 struct EpiGrad {
@@ -84,6 +100,12 @@ struct EpiGrad {
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
     const int N = *count;
     const float s = N > 0 ? tau / (float)N : 0.f;
+    // Rows past the vocabulary (z = 0 from zero-filled A rows) get finite
+    // junk here: the head-gradient GEMM never reads G^T rows >= V, and the
+    // hidden-gradient GEMM multiplies G's columns >= V by the zero columns of
+    // the padded W^T.  Capping the exponent at 0 keeps them finite (for real
+    // rows x*c2 <= lse2 holds exactly, since both passes produce the same z
+    // and the merged sum is >= 1).
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = c.n0 + 32 * j + acc_col(c.lane);
@@ -99,10 +121,7 @@ struct EpiGrad {
           const int v0 = c.m0 + 32 * i + 8 * g4 + 4 * (c.lane >> 5);
           float gv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = acc[i][j][4 * g4 + e];
-            gv[e] = (sc != 0.f && v0 + e < V) ? sc * fast_exp2(x * c2 - l2) : 0.f;
-          }
+          for (int e = 0; e < 4; ++e) gv[e] = sc * fast_exp2(fminf(acc[i][j][4 * g4 + e] * c2 - l2, 0.f));
           store4(G + (int64_t)n * ldg + v0, gv);
 #pragma unroll
           for (int e = 0; e < 4; ++e) Gt[(int64_t)(v0 + e) * ldgt + n] = store_cvt<E>(gv[e]);
@@ -154,24 +173,42 @@ struct EpiAccum {
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    const bool full = c.m0 + FM * 32 <= M && c.n0 + FN * 32 <= N;
+    if (full) {
+      // old values first (one burst of loads), then the stores
+      if (!first) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const float* p = out + (int64_t)(c.m0 + 32 * i) * ld + c.n0 + 32 * j + acc_col(c.lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] += p[(int64_t)acc_row(r, c.lane) * ld];
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          float* p = out + (int64_t)(c.m0 + 32 * i) * ld + c.n0 + 32 * j + acc_col(c.lane);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[(int64_t)acc_row(r, c.lane) * ld] = acc[i][j][r];
+        }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int n = c.n0 + 32 * j + acc_col(c.lane);
         if (n >= N) continue;
-        float old[16];
-        if (!first) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = c.m0 + 32 * i + acc_row(r, c.lane);
-            old[r] = m < M ? out[(int64_t)m * ld + n] : 0.f;
-          }
-        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = c.m0 + 32 * i + acc_row(r, c.lane);
-          if (m < M) out[(int64_t)m * ld + n] = first ? acc[i][j][r] : old[r] + acc[i][j][r];
+          if (m < M) {
+            float* p = out + (int64_t)m * ld + n;
+            *p = first ? acc[i][j][r] : *p + acc[i][j][r];
+          }
         }
       }
   }

@@ -31,12 +31,22 @@
 namespace kd {
 namespace {
 
-// GEMM tile configuration shared by the four contractions: 256 x 256 block
-// tiles, 8 waves as 2 (M) x 4 (N), each wave 128 x 64; 3 LDS stages of 64
-// bytes of K (96 KB of LDS).
-constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4, kStages = 3;
-constexpr int kWaveM = kBM / kWM;     // vocabulary strip of one LSE partial
-constexpr int kThreads = 64 * kWM * kWN;
+// GEMM tile configurations (block tile BM x BN, WM x WN waves, LDS stages of
+// 64 bytes of K), chosen by measurement on MI355X:
+//  - the logit GEMMs and the hidden-gradient GEMM: 256 x 256, 8 waves of
+//    128 x 64, 3 stages (96 KB LDS, one block per CU);
+//  - the head-gradient GEMM, whose epilogue reads and writes the fp32 grad_W
+//    tile: 256 x 128, 8 waves of 64 x 64, 3 stages (72 KB LDS, two blocks per
+//    CU, so one block's read-modify-write overlaps the other's MFMAs).
+template <int BM_, int BN_, int WM_, int WN_, int ST_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_;
+  static constexpr int kThreads = 64 * WM * WN;
+};
+using TileMain = TileCfg<256, 256, 2, 4, 3>;
+using TileHead = TileCfg<256, 128, 4, 2, 3>;
+constexpr int kBM = TileMain::BM, kBN = TileMain::BN;
+constexpr int kWaveM = TileMain::BM / TileMain::WM;   // vocabulary strip of one LSE partial
 constexpr int kKStep = 64;            // bytes of K per pipeline stage
 constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
 
@@ -92,7 +102,9 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
     if (k_tiles / sp < 16) cost += 1.0;                     // splits too thin
     if (cost < best_cost) { best_cost = cost; best = sp; }
   }
-  P.splits = best;
+  // every split must own at least one K stage
+  const int64_t kps = cdiv(k_tiles, best);
+  P.splits = (int)cdiv(k_tiles, kps);
 
   const size_t e = (size_t)P.eb;
   size_t o = 0;
@@ -111,24 +123,26 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   return KD_OK;
 }
 
-template <class E, class Epi>
+// One block per tile (a multiple of 8 blocks).
+template <class TC, class E, class Epi>
 hipError_t launch_gemm(const GemmShape& g, const Epi& epi, hipStream_t st) {
   const int nb = g.tiles_m * g.tiles_n * g.splits;
   const int grid = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_nt_kernel<E, kBM, kBN, kWM, kWN, kStages, Epi>), dim3(grid), dim3(kThreads), 0, st, g,
-                     epi);
+  hipLaunchKernelGGL((gemm_nt_kernel<E, TC::BM, TC::BN, TC::WM, TC::WN, TC::STAGES, Epi>), dim3(grid),
+                     dim3(TC::kThreads), 0, st, g, epi);
   return hipGetLastError();
 }
 
+template <class TC>
 GemmShape make_shape(const void* A, int64_t lda, int M, const void* B, int64_t ldb, int N, int64_t k_bytes,
                      int splits) {
   GemmShape g;
   g.A = A; g.B = B; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N;
   g.k_tiles = (int)(k_bytes / kKStep);
-  g.splits = splits;
   g.k_tiles_per_split = (int)cdiv(g.k_tiles, splits);
-  g.tiles_m = (int)cdiv(M, kBM);
-  g.tiles_n = (int)cdiv(N, kBN);
+  g.splits = (int)cdiv(g.k_tiles, g.k_tiles_per_split);   // <= splits; no split is empty
+  g.tiles_m = (int)cdiv(M, TC::BM);
+  g.tiles_n = (int)cdiv(N, TC::BN);
   return g;
 }
 
@@ -213,9 +227,9 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     // forward: z^T = W H_c^T -> LSE partials
     mark(slot + 1, 0);
     {
-      GemmShape g = make_shape(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
+      GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
       EpiLsePartial epi{part, (int)P.R_p, (int)V, c2};
-      if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 1, 1);
     mark(slot + 2, 0);
@@ -229,9 +243,9 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     mark(slot + 3, 0);
     // backward recompute: G = (tau/N) m q, both layouts
     {
-      GemmShape g = make_shape(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
+      GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
       EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse2, mask_c, count, tau, c2, (int)V, R};
-      if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 3, 1);
     mark(slot + 4, 0);
@@ -242,23 +256,23 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     mark(slot + 5, 0);
     // dH_c = G W  (A = G [Rt x V_p], B = W^T [d x V_p]), split-K over V
     {
-      GemmShape g = make_shape(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits);
+      GemmShape g = make_shape<TileMain>(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits);
       EpiStoreSplit epi{dhp, P.Nd_p, P.R_p * P.Nd_p};
-      if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
       mark(slot + 5, 1);
       mark(slot + 6, 0);
       const int64_t n = (int64_t)R * d;
       hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
-                         (const float*)dhp, P.Nd_p, P.R_p * P.Nd_p, P.splits, R, (int)d, grad_hidden + c0 * d, d);
+                         (const float*)dhp, P.Nd_p, P.R_p * P.Nd_p, g.splits, R, (int)d, grad_hidden + c0 * d, d);
       KD_LAUNCH_CHECK();
       mark(slot + 6, 1);
     }
     mark(slot + 7, 0);
     // dW (+)= G^T H_c  (A = G^T [V_p x R_p], B = H_c^T [d x R_p])
     {
-      GemmShape g = make_shape(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1);
+      GemmShape g = make_shape<TileHead>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1);
       EpiAccum epi{grad_W, d, (int)V, (int)d, c == 0 ? 1 : 0};
-      if (launch_gemm<E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 7, 1);
   }
