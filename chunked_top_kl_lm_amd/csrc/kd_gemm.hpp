@@ -136,8 +136,15 @@ struct EpiCtx {
 // makes every wave's LDS writes visible; the stage overwritten next is the
 // one all waves finished reading before that same barrier.
 // ---------------------------------------------------------------------------
-// 16-byte slot permutation of a 64-byte LDS row r (see above).
-__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+// 16-byte slot permutation of an LDS row r of RB bytes (see above): for
+// 64-byte rows f(r) = (r >> 2) & 3, for 128-byte rows f(r) = (r >> 1) & 7
+// (both measured conflict-free for the MFMA fragment reads).
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(RB == 64 || RB == 128, "row bytes");
+  return RB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+__device__ __forceinline__ int swz64(int r) { return swz<64>(r); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -151,21 +158,24 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <class E, int BM, int BN, int WM, int WN, int STAGES>
+template <class E, int BM, int BN, int WM, int WN, int STAGES, int RB_ = 64>
 struct PipeCfg {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int RB = 64;
+  static constexpr int RB = RB_;                // bytes of K per row per stage
+  static constexpr int GROUPS = RB / 32;        // 32-byte K groups per stage
+  static constexpr int RPD = 1024 / RB;         // rows per 1 KB DMA instruction
   static constexpr int kStage = (BM + BN) * RB;
   static constexpr int kLds = STAGES * kStage;
-  static constexpr int IA = BM / 16 / NW;     // DMA instructions per wave per stage (A)
-  static constexpr int IB = BN / 16 / NW;
+  static constexpr int IA = BM / RPD / NW;      // DMA instructions per wave per stage (A)
+  static constexpr int IB = BN / RPD / NW;
   static constexpr int kPer = IA + IB;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert((BM / 16) % NW == 0 && (BN / 16) % NW == 0, "DMA split");
+  static_assert((BM / RPD) % NW == 0 && (BN / RPD) % NW == 0, "DMA split");
   static_assert(STAGES >= 2 && (STAGES - 1) * (IA + IB) < 64, "vmcnt range");
+  static_assert(GROUPS % 2 == 0, "fragment ping-pong needs an even group count");
 };
 
 template <class C, int BM>
@@ -215,13 +225,66 @@ __device__ __forceinline__ void mfma_all(f32x16 (&acc)[C::FM][C::FN], const u32x
     for (int j = 0; j < C::FN; ++j) mfma_group<E>(acc[i][j], fa[i], fb[j]);
 }
 
+// Interleave hints for one K-group: MFMAs alternate with `reads` DS reads
+// and, for the group that carries the stage refill, with the DMA issues.
+template <class C, int ID, bool DMA>
+__device__ __forceinline__ void sched_group_hints() {
+  if constexpr (DMA) {
+#pragma unroll
+    for (int z = 0; z < C::kPer; ++z) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, ID);  // 1 VMEM (DMA)
+    }
+  }
+#pragma unroll
+  for (int z = 0; z < C::FM + C::FN; ++z) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);    // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);    // 1 DS read
+  }
+}
+
+// One K stage of the main loop (see gemm_nt_kernel).  MORE: another stage
+// follows, so this one ends with the wait / barrier / refill / prefetch.
+template <class E, class C, int BM, int STAGES, bool MORE>
+__device__ __forceinline__ void gemm_stage(f32x16 (&acc)[C::FM][C::FN], u32x4 (&fa)[2][C::FM], u32x4 (&fb)[2][C::FN],
+                                           char* smem, int it, uint32_t aRow0, uint32_t bRow0,
+                                           const uint32_t (&uoff)[C::GROUPS], __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rb, const uint32_t* voffA, const uint32_t* voffB,
+                                           int wid, uint32_t refill_ko) {
+  const char* s = smem + (it % STAGES) * C::kStage;
+#pragma unroll
+  for (int q = 0; q < C::GROUPS; ++q) {
+    const int cur = q & 1, nxt = cur ^ 1;
+    if (q + 1 < C::GROUPS) {
+      read_frags<C>(s, aRow0, bRow0, uoff[q + 1], fa[nxt], fb[nxt]);
+    } else if constexpr (MORE) {
+      // this wave's reads of stage `it` have returned; stage it+1 has landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+      wait_vmcnt<(STAGES - 2) * C::kPer>();
+      lds_barrier();
+      dma_stage<C, BM>(smem + (it % STAGES) * C::kStage, ra, rb, voffA, voffB, wid, refill_ko);
+      read_frags<C>(smem + ((it + 1) % STAGES) * C::kStage, aRow0, bRow0, uoff[0], fa[nxt], fb[nxt]);
+    }
+    mfma_all<E, C>(acc, fa[cur], fb[cur]);
+    if (q + 1 == C::GROUPS) sched_group_hints<C, 2 * C::GROUPS, MORE>();
+    else sched_group_hints<C, 2 * C::GROUPS, false>();
+  }
+}
+
 // One block per output tile (grid = all tiles, rounded up to a multiple of
 // 8): the dispatcher hands a CU its next tile as soon as the previous one
-// ends.  Used where the epilogue is light; gemm_nt_kernel (persistent) is
-// used where the epilogue has to overlap with the next tile's loads.
-template <class E, int BM, int BN, int WM, int WN, int STAGES, class Epi>
+// ends.  With the 96 KB LDS ring of a 256 x 256 tile one block fits per CU;
+// with the 72 KB ring of a 256 x 128 tile two blocks share a CU, so one
+// block's epilogue overlaps the other's main loop.
+//
+// Each stage holds RB bytes of K (GROUPS = RB/32 K-groups).  Fragments are
+// read one group ahead into a second register set; before the last group's
+// MFMAs the wave waits for its own reads and for the next stage's DMA,
+// passes the barrier, refills the buffer it has just consumed, and reads
+// group 0 of the next stage.
+template <class E, int BM, int BN, int WM, int WN, int STAGES, class Epi, int RB = 64>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi epi) {
-  typedef PipeCfg<E, BM, BN, WM, WN, STAGES> C;
+  typedef PipeCfg<E, BM, BN, WM, WN, STAGES, RB> C;
   __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
 
   const TilePos pos = tile_position(g);
@@ -232,6 +295,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
   const int wid = tid >> 6;
   const int wm = wid / WN, wn = wid - (wid / WN) * WN;
 
+  // g.k_tiles counts RB-byte K stages
   const int kt0 = pos.split * g.k_tiles_per_split;
   int kt1 = kt0 + g.k_tiles_per_split;
   if (kt1 > g.k_tiles) kt1 = g.k_tiles;
@@ -240,21 +304,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
   const int rowsA = min(BM, g.M - pos.tm * BM);
   const int rowsB = min(BN, g.N - pos.tn * BN);
   const int64_t strideA = g.lda * E::kBytes, strideB = g.ldb * E::kBytes;
-  const char* baseA = (const char*)g.A + (int64_t)pos.tm * BM * strideA + (int64_t)kt0 * C::RB;
-  const char* baseB = (const char*)g.B + (int64_t)pos.tn * BN * strideB + (int64_t)kt0 * C::RB;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(baseA, (uint32_t)(rowsA * strideA - kt0 * C::RB));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(baseB, (uint32_t)(rowsB * strideB - kt0 * C::RB));
+  const char* baseA = (const char*)g.A + (int64_t)pos.tm * BM * strideA + (int64_t)kt0 * RB;
+  const char* baseB = (const char*)g.B + (int64_t)pos.tn * BN * strideB + (int64_t)kt0 * RB;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(baseA, (uint32_t)(rowsA * strideA - kt0 * RB));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(baseB, (uint32_t)(rowsB * strideB - kt0 * RB));
 
+  // DMA source offsets: lane fills slot (lane % UPR) of row r = RPD*j +
+  // lane / UPR of the stage (j = wid + NW*i); that slot holds logical unit
+  // slot ^ f(r).
+  constexpr int UPR = RB / 16;                             // 16-byte units per row
   uint32_t voffA[C::IA], voffB[C::IB];
 #pragma unroll
   for (int i = 0; i < C::IA; ++i) {
-    const int r = 16 * (wid + C::NW * i) + (lane >> 2);
-    voffA[i] = (uint32_t)(r * strideA + (((lane & 3) ^ swz64(r)) << 4));
+    const int r = C::RPD * (wid + C::NW * i) + lane / UPR;
+    voffA[i] = (uint32_t)(r * strideA + (((lane % UPR) ^ swz<RB>(r)) << 4));
   }
 #pragma unroll
   for (int i = 0; i < C::IB; ++i) {
-    const int r = 16 * (wid + C::NW * i) + (lane >> 2);
-    voffB[i] = (uint32_t)(r * strideB + (((lane & 3) ^ swz64(r)) << 4));
+    const int r = C::RPD * (wid + C::NW * i) + lane / UPR;
+    voffB[i] = (uint32_t)(r * strideB + (((lane % UPR) ^ swz<RB>(r)) << 4));
   }
 
   f32x16 acc[C::FM][C::FN];
@@ -265,58 +333,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // fragment reads: row (lane & 31) of a 32-row MFMA tile, logical unit
+  // 2*group + (lane >> 5), at slot unit ^ f(row); f is the same for every
+  // 32-row tile of the wave
   const int frow = lane & 31, fhalf = lane >> 5;
-  const int fsw = swz64(wm * C::TM + frow);
-  const uint32_t aRow0 = (uint32_t)((wm * C::TM + frow) * C::RB);
-  const uint32_t bRow0 = (uint32_t)(BM * C::RB + (wn * C::TN + frow) * C::RB);
-  const uint32_t uoff0 = (uint32_t)(((0 + fhalf) ^ fsw) << 4);
-  const uint32_t uoff1 = (uint32_t)(((2 + fhalf) ^ fsw) << 4);
+  const int fsw = swz<RB>(wm * C::TM + frow);
+  const uint32_t aRow0 = (uint32_t)((wm * C::TM + frow) * RB);
+  const uint32_t bRow0 = (uint32_t)(BM * RB + (wn * C::TN + frow) * RB);
+  uint32_t uoff[C::GROUPS];
+#pragma unroll
+  for (int q = 0; q < C::GROUPS; ++q) uoff[q] = (uint32_t)(((2 * q + fhalf) ^ fsw) << 4);
 
   // Stages past the end of K are still issued, at an offset beyond the
   // buffer range: the hardware returns zeros without a memory access.  Every
   // iteration thus issues exactly one stage and the vmcnt bookkeeping is the
   // same constant in all of them.
-  auto kofs = [&](int kt) -> uint32_t { return kt < nk ? (uint32_t)kt * C::RB : 0x80000000u; };
+  auto kofs = [&](int kt) -> uint32_t { return kt < nk ? (uint32_t)kt * RB : 0x80000000u; };
 
-  u32x4 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+  u32x4 fa[2][C::FM], fb[2][C::FN];
   if (nk > 0) {
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) dma_stage<C, BM>(smem + st * C::kStage, ra, rb, voffA, voffB, wid, kofs(st));
     wait_vmcnt<(STAGES - 1) * C::kPer>();                  // stage 0 has landed
     lds_barrier();
-    read_frags<C>(smem, aRow0, bRow0, uoff0, fa0, fb0);
+    read_frags<C>(smem, aRow0, bRow0, uoff[0], fa[0], fb[0]);
 
-    for (int it = 0; it < nk - 1; ++it) {
-      const char* s = smem + (it % STAGES) * C::kStage;
-      read_frags<C>(s, aRow0, bRow0, uoff1, fa1, fb1);
-      mfma_all<E, C>(acc, fa0, fb0);
-#pragma unroll
-      for (int q = 0; q < C::FM + C::FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-      }
-      // this wave's reads of stage `it` have returned; stage it+1 has landed
-      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
-      wait_vmcnt<(STAGES - 2) * C::kPer>();
-      lds_barrier();
-      dma_stage<C, BM>(smem + (it % STAGES) * C::kStage, ra, rb, voffA, voffB, wid, kofs(it + STAGES));
-      read_frags<C>(smem + ((it + 1) % STAGES) * C::kStage, aRow0, bRow0, uoff0, fa0, fb0);
-      mfma_all<E, C>(acc, fa1, fb1);
-#pragma unroll
-      for (int q = 0; q < C::kPer; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 VMEM (DMA)
-      }
-#pragma unroll
-      for (int q = 0; q < C::FM + C::FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      }
-    }
-    // last stage
-    read_frags<C>(smem + ((nk - 1) % STAGES) * C::kStage, aRow0, bRow0, uoff1, fa1, fb1);
-    mfma_all<E, C>(acc, fa0, fb0);
-    mfma_all<E, C>(acc, fa1, fb1);
+    for (int it = 0; it < nk - 1; ++it)
+      gemm_stage<E, C, BM, STAGES, true>(acc, fa, fb, smem, it, aRow0, bRow0, uoff, ra, rb, voffA, voffB, wid,
+                                         kofs(it + STAGES));
+    gemm_stage<E, C, BM, STAGES, false>(acc, fa, fb, smem, nk - 1, aRow0, bRow0, uoff, ra, rb, voffA, voffB, wid, 0u);
     wait_vmcnt<0>();                                       // drain the tail loads before LDS is reused
   }
   lds_barrier();

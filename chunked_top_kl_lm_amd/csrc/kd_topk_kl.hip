@@ -31,23 +31,24 @@
 namespace kd {
 namespace {
 
-// GEMM tile configurations (block tile BM x BN, WM x WN waves, LDS stages of
-// 64 bytes of K), chosen by measurement on MI355X:
+// GEMM tile configurations (block tile BM x BN, WM x WN waves, STAGES LDS
+// stages of RB bytes of K), chosen by measurement on MI355X:
 //  - the logit GEMMs and the hidden-gradient GEMM: 256 x 256, 8 waves of
-//    128 x 64, 3 stages (96 KB LDS, one block per CU);
+//    128 x 64, 2 stages of 128 bytes (128 KB LDS, one block per CU; half the
+//    barriers of 64-byte stages);
 //  - the head-gradient GEMM, whose epilogue reads and writes the fp32 grad_W
-//    tile: 256 x 128, 8 waves of 64 x 64, 3 stages (72 KB LDS, two blocks per
-//    CU, so one block's read-modify-write overlaps the other's MFMAs).
-template <int BM_, int BN_, int WM_, int WN_, int ST_>
+//    tile: 256 x 128, 8 waves of 64 x 64, 3 stages of 64 bytes (72 KB LDS,
+//    two blocks per CU, so one block's read-modify-write overlaps the other's
+//    MFMAs).
+template <int BM_, int BN_, int WM_, int WN_, int ST_, int RB_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_, RB = RB_;
   static constexpr int kThreads = 64 * WM * WN;
 };
-using TileMain = TileCfg<256, 256, 2, 4, 3>;
-using TileHead = TileCfg<256, 128, 4, 2, 3>;
+using TileMain = TileCfg<256, 256, 2, 4, 2, 128>;
+using TileHead = TileCfg<256, 128, 4, 2, 3, 64>;
 constexpr int kBM = TileMain::BM, kBN = TileMain::BN;
 constexpr int kWaveM = TileMain::BM / TileMain::WM;   // vocabulary strip of one LSE partial
-constexpr int kKStep = 64;            // bytes of K per pipeline stage
 constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -91,7 +92,7 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   // two waves when the K extent allows, and a small penalty per split for
   // the partial-sum traffic.
   const int64_t tiles = cdiv(P.R_p, kBM) * cdiv(P.Nd_p, kBN);
-  const int64_t k_tiles = P.V_p * P.eb / kKStep;
+  const int64_t k_tiles = P.V_p * P.eb / TileMain::RB;
   int best = 1;
   double best_cost = 1e30;
   for (int sp = 1; sp <= 64 && sp <= k_tiles; ++sp) {
@@ -128,7 +129,7 @@ template <class TC, class E, class Epi>
 hipError_t launch_gemm(const GemmShape& g, const Epi& epi, hipStream_t st) {
   const int nb = g.tiles_m * g.tiles_n * g.splits;
   const int grid = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_nt_kernel<E, TC::BM, TC::BN, TC::WM, TC::WN, TC::STAGES, Epi>), dim3(grid),
+  hipLaunchKernelGGL((gemm_nt_kernel<E, TC::BM, TC::BN, TC::WM, TC::WN, TC::STAGES, Epi, TC::RB>), dim3(grid),
                      dim3(TC::kThreads), 0, st, g, epi);
   return hipGetLastError();
 }
@@ -138,7 +139,7 @@ GemmShape make_shape(const void* A, int64_t lda, int M, const void* B, int64_t l
                      int splits) {
   GemmShape g;
   g.A = A; g.B = B; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N;
-  g.k_tiles = (int)(k_bytes / kKStep);
+  g.k_tiles = (int)(k_bytes / TC::RB);
   g.k_tiles_per_split = (int)cdiv(g.k_tiles, splits);
   g.splits = (int)cdiv(g.k_tiles, g.k_tiles_per_split);   // <= splits; no split is empty
   g.tiles_m = (int)cdiv(M, TC::BM);
