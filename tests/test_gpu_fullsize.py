@@ -1,0 +1,116 @@
+"""Full-size workloads on the GPU, in the launch configuration bench.py times.
+
+At T = 32768 / 131072 / 262144 the oracle cannot form every row's full
+vocabulary, so these tests check:
+  - sampled rows (first, last, masked, random) of row_lse, row_kl and
+    grad_hidden against the oracle's per-row results, element by element;
+  - the loss against tau^2 * sum_t m_t KL_t / N recomputed in fp64 from the
+    library's own per-row KL (the reduction), and finite/positive;
+  - properties that hold at any size: zero column sums of grad_W
+    (sum_v G[t,v] = 0), <grad_hidden, H> = <grad_W, W> (both equal sum G.Z),
+    masked rows of grad_hidden exactly zero;
+  - the workspace and the peak device memory beyond the O(T) buffers do not
+    depend on T.
+The reduced-T tests in test_gpu_parity.py check grad_W element by element at
+these d and V.
+"""
+import numpy as np
+import pytest
+
+from datagen import config_for, make_inputs
+from oracle import fused_kl_rows
+from tests.gpu_util import GRAD_TOL, LOSS_TOL, log, rel, rel_f, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_full(num, T=None):
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    cfg = config_for(num, **({"T": T} if T else {}))
+    log(f"[gpu-full] generating workload {num} T={cfg.T}")
+    x = make_inputs(cfg, seed=0, topk_backend="torch-cuda")
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    t = to_device(x)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    log(f"[gpu-full] workload {num}: T={cfg.T} chunk={cfg.chunk} tau={cfg.tau}")
+    loss, gH, gW, rl, rk = kd.fwd_bwd(t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"],
+                                      tau=cfg.tau, chunk=cfg.chunk, row_stats=True, status=st)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    out = dict(loss=float(loss.item()), status=int(st.item()), peak=peak,
+               gH=gH, gW=gW, row_lse=rl.cpu().numpy(), row_kl=rk.cpu().numpy(), t=t)
+    return x, cfg, out
+
+
+def _checks(x, cfg, out, n_random=6):
+    import torch
+    T = cfg.T
+    assert out["status"] == 0
+    mask = x["mask"]
+    # the loss is the tau^2-scaled masked mean of the per-row KL
+    m = mask.astype(np.float64)
+    want = cfg.tau ** 2 * float((m * out["row_kl"].astype(np.float64)).sum()) / m.sum()
+    assert np.isfinite(out["loss"]) and out["loss"] > 0
+    assert rel(out["loss"], want) < 1e-5
+    # sampled rows against the oracle
+    rng = np.random.default_rng(123)
+    masked = np.nonzero(mask == 0)[0]
+    rows = sorted(set([0, T - 1, int(masked[0]), int(masked[-1])] + rng.integers(0, T, n_random).tolist()))
+    log(f"[gpu-full] oracle rows {rows}")
+    ref = fused_kl_rows(x["hidden"], x["W"], x["teacher_idx"], x["teacher_logit"], mask, cfg.tau, rows)
+    gH_rows = out["gH"][torch.tensor(rows, device="cuda:0")].cpu().numpy()
+    e_lse = np.max(np.abs(out["row_lse"][rows] - ref["row_lse"]))
+    e_kl = np.max(np.abs(out["row_kl"][rows] - ref["row_kl"]) / np.maximum(1.0, np.abs(ref["row_kl"])))
+    live = [i for i, r in enumerate(rows) if mask[r]]
+    e_gh = rel_f(gH_rows[live], ref["grad_hidden_rows"][live])
+    log(f"[gpu-full] max|dLSE| {e_lse:.2e}  max rel dKL {e_kl:.2e}  sampled dH relF {e_gh:.2e}")
+    assert e_lse < 1e-3
+    assert e_kl < LOSS_TOL
+    assert e_gh < GRAD_TOL
+    dead = [i for i, r in enumerate(rows) if not mask[r]]
+    assert np.all(gH_rows[dead] == 0)
+    # properties of the full gradients (fp64 reductions on the device)
+    gW = out["gW"].double()
+    colsum = gW.sum(0)
+    cs = float(torch.linalg.norm(colsum) / torch.linalg.norm(gW.abs().sum(0)))
+    hid = out["t"]["hidden"].double()
+    Wd = out["t"]["W"].double()
+    a = float((out["gH"].double() * hid).sum())
+    b = float((gW * Wd).sum())
+    log(f"[gpu-full] column-sum ratio {cs:.2e}  <dH,H> {a:.6e}  <dW,W> {b:.6e}")
+    assert cs < 1e-2
+    assert rel(a, b) < GRAD_TOL
+
+
+def test_gptoss_32k_full():
+    x, cfg, out = _run_full(3)
+    _checks(x, cfg, out)
+
+
+def test_long_128k_full_tau2():
+    x, cfg, out = _run_full(4)
+    _checks(x, cfg, out)
+
+
+def test_extreme_256k_full_and_memory_is_t_independent():
+    import chunked_top_kl_lm_amd as kd
+    x, cfg, out = _run_full(5)
+    _checks(x, cfg, out, n_random=4)
+    peak_256k = out["peak"]
+    del out, x
+    import torch
+    torch.cuda.empty_cache()
+    # the same head at T = 32768 with the same chunk
+    x2, cfg2, out2 = _run_full(5, T=32768)
+    peak_32k = out2["peak"]
+    d, V, K = cfg.d, cfg.V, cfg.K
+    # O(T) buffers: hidden (bf16) + grad_hidden (fp32) + idx + logit + mask + 2 row stats + loss/status
+    per_token = 2 * d + 4 * d + 4 * K + 4 * K + 1 + 4 + 4
+    extra = (peak_256k - peak_32k) - per_token * (cfg.T - cfg2.T)
+    log(f"[gpu-full] peak {peak_32k / 2**30:.2f} GiB at T=32768, {peak_256k / 2**30:.2f} GiB at T=262144; "
+        f"difference beyond the O(T) buffers {extra / 2**20:.1f} MiB")
+    assert abs(extra) < 64 * 2**20
+    assert kd.workspace_bytes(262144, d, V, K, cfg.chunk, kd.KD_BF16) == kd.workspace_bytes(32768, d, V, K, cfg.chunk, kd.KD_BF16)
