@@ -88,11 +88,15 @@ struct GemmShape {
   int k_tiles;        // 128-byte K steps in the whole product
   int k_tiles_per_split;
   int tiles_m, tiles_n, splits;
+  int group_m;        // tile order: groups of group_m row tiles x all column tiles
 };
 
-// Position of this block's tile.  Blocks are dispatched round-robin over the
-// 8 XCDs; consecutive logical tiles are sent to the same XCD so that the
-// blocks sharing an A tile (same m, consecutive n) hit the same L2.
+// Position of this block's tile.  Linear tile order: split-K slice, then
+// groups of group_m row tiles x all column tiles, row index fastest inside a
+// group, so that a window of consecutive tiles shares both its A and B
+// tiles.  Blocks are dispatched round-robin over the 8 XCDs; each XCD is
+// given one contiguous range of that order, so the blocks an XCD runs at
+// the same time share their operands in its L2.
 struct TilePos { int tm, tn, split; bool valid; };
 
 __device__ __forceinline__ TilePos tile_position(const GemmShape& g) {
@@ -104,8 +108,12 @@ __device__ __forceinline__ TilePos tile_position(const GemmShape& g) {
   const int mn = g.tiles_m * g.tiles_n;
   p.split = lin / mn;
   const int r = lin - p.split * mn;
-  p.tm = r / g.tiles_n;
-  p.tn = r - p.tm * g.tiles_n;
+  const int span = g.group_m * g.tiles_n;      // tiles per full group
+  const int grp = r / span;
+  const int w = r - grp * span;
+  const int gm = min(g.group_m, g.tiles_m - grp * g.group_m);
+  p.tm = grp * g.group_m + w % gm;
+  p.tn = w / gm;
   return p;
 }
 

@@ -134,10 +134,14 @@ hipError_t launch_gemm(const GemmShape& g, const Epi& epi, hipStream_t st) {
   return hipGetLastError();
 }
 
+// group_m: row tiles per group of the tile order (see tile_position).  The
+// head-gradient GEMM uses 4 (it re-streams its 11.8 MB H_c^T operand once
+// per row band otherwise); the others measured best with 1.
 template <class TC>
 GemmShape make_shape(const void* A, int64_t lda, int M, const void* B, int64_t ldb, int N, int64_t k_bytes,
-                     int splits) {
+                     int splits, int group_m) {
   GemmShape g;
+  g.group_m = group_m;
   g.A = A; g.B = B; g.lda = lda; g.ldb = ldb; g.M = M; g.N = N;
   g.k_tiles = (int)(k_bytes / TC::RB);
   g.k_tiles_per_split = (int)cdiv(g.k_tiles, splits);
@@ -228,7 +232,7 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     // forward: z^T = W H_c^T -> LSE partials
     mark(slot + 1, 0);
     {
-      GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
+      GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
       EpiLsePartial epi{part, (int)P.R_p, (int)V, c2};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
@@ -244,7 +248,7 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     mark(slot + 3, 0);
     // backward recompute: G = (tau/N) m q, both layouts
     {
-      GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1);
+      GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
       EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse2, mask_c, count, tau, c2, (int)V, R};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
@@ -257,7 +261,7 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     mark(slot + 5, 0);
     // dH_c = G W  (A = G [Rt x V_p], B = W^T [d x V_p]), split-K over V
     {
-      GemmShape g = make_shape<TileMain>(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits);
+      GemmShape g = make_shape<TileMain>(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits, 8);
       EpiStoreSplit epi{dhp, P.Nd_p, P.R_p * P.Nd_p};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
       mark(slot + 5, 1);
@@ -271,7 +275,7 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     mark(slot + 7, 0);
     // dW (+)= G^T H_c  (A = G^T [V_p x R_p], B = H_c^T [d x R_p])
     {
-      GemmShape g = make_shape<TileHead>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1);
+      GemmShape g = make_shape<TileHead>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
       EpiAccum epi{grad_W, d, (int)V, (int)d, c == 0 ? 1 : 0};
       if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
