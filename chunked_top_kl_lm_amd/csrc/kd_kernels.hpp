@@ -310,6 +310,44 @@ __global__ __launch_bounds__(256) void pad_kernel(const typename E::T* src, int6
   }
 }
 
+
+// Online logsumexp across vocabulary strips: for each chunk row t, merge the
+// per-strip (max, sum exp2) partials into the row's normaliser
+// lse2[t] = log2 sum_v exp2(z[t,v] log2(e) / tau).  Block = 32 rows x 8
+// strip slices; consecutive threads read consecutive rows of one strip
+// (coalesced); the 8 slices are merged in a fixed order.
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float2* part, int ldp, int nvt, int R, float* lse2_out,
+                                                        float* row_lse) {
+  __shared__ float s_m[8][32];
+  __shared__ float s_l[8][32];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int t = blockIdx.x * 32 + tx;
+  float M = -INFINITY, L = 0.f;
+  if (t < R) {
+    for (int vt = ty; vt < nvt; vt += 8) {
+      const float2 p = part[(int64_t)vt * ldp + t];
+      if (p.y <= 0.f) continue;               // strip with no vocabulary rows
+      if (p.x > M) { L = L * fast_exp2(M - p.x) + p.y; M = p.x; }
+      else L += p.y * fast_exp2(p.x - M);
+    }
+  }
+  s_m[ty][tx] = M;
+  s_l[ty][tx] = L;
+  __syncthreads();
+  if (ty == 0 && t < R) {
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      const float m2 = s_m[q][tx], l2 = s_l[q][tx];
+      if (l2 <= 0.f) continue;
+      if (m2 > M) { L = L * fast_exp2(M - m2) + l2; M = m2; }
+      else L += l2 * fast_exp2(m2 - M);
+    }
+    const float lse2 = M + __log2f(L);
+    lse2_out[t] = lse2;
+    if (row_lse) row_lse[t] = lse2 * kLn2;    // natural-log normaliser of S = z / tau
+  }
+}
+
 template <class E> __device__ __forceinline__ float dot16(u32x4 a, u32x4 b);
 template <> __device__ __forceinline__ float dot16<Bf16>(u32x4 a, u32x4 b) {
   float s = 0.f;
@@ -326,76 +364,87 @@ template <> __device__ __forceinline__ float dot16<F32>(u32x4 a, u32x4 b) {
 }
 
 // One block per chunk row t:
-//  1. merge the per-strip (max, sum) partials into the row's logsumexp
-//     (online logsumexp across vocabulary tiles);
-//  2. the teacher's distribution p over its K cached ids;
-//  3. the student logits at those ids, z_k = h_t . W[idx_k] (gathered rows);
-//  4. KL_t = sum_k p_k (log p_k - (z_k / tau - LSE_t)).
+//  1. the teacher's distribution p over its K cached ids;
+//  2. the student logits at those ids, z_k = h_t . W[idx_k] (gathered W
+//     rows; each wave takes four ids at a time so that four rows' loads are
+//     in flight; the hidden row is held in registers);
+//  3. KL_t = sum_k p_k (log p_k - (z_k / tau - LSE_t)).
 // Invalid ids set *status and contribute nothing.
+constexpr int kGatherIds = 4;     // ids per wave per step
+constexpr int kMaxUnits = 12;     // 16-byte units of the hidden row held per lane (the first 12 KB)
+
 template <class E>
 __global__ __launch_bounds__(256) void kl_rows_kernel(
-    const float2* part, int ldp, int nvt,
-    const typename E::T* hsrc, int64_t ldh, const typename E::T* wsrc, int64_t ldw, int units16,
-    const int32_t* idx, const float* logit, int K, int V, float tau,
-    float* lse2_out, double* rowkl, float* row_lse, float* row_kl, int32_t* status) {
+    const float* lse2_in, const typename E::T* hsrc, int64_t ldh, const typename E::T* wsrc, int64_t ldw,
+    int units16, const int32_t* idx, const float* logit, int K, int V, float tau, double* rowkl, float* row_kl,
+    int32_t* status) {
   __shared__ float s_a[kMaxK];
   __shared__ float s_z[kMaxK];
-  __shared__ float s_m[256];
-  __shared__ float s_l[256];
+  __shared__ float s_red[256];
   __shared__ double s_d[256];
   const int t = blockIdx.x, tid = threadIdx.x;
+  const float lse = lse2_in[t] * kLn2;        // natural-log normaliser of S = z / tau
 
-  // 1. online merge of the vocabulary-strip partials (fixed order)
-  float M = -INFINITY, L = 0.f;
-  for (int vt = tid; vt < nvt; vt += 256) {
-    const float2 p = part[(int64_t)vt * ldp + t];
-    if (p.x == -INFINITY) continue;
-    if (p.x > M) { L = L * fast_exp2(M - p.x) + p.y; M = p.x; }
-    else L += p.y * fast_exp2(p.x - M);
-  }
-  s_m[tid] = M; s_l[tid] = L;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) {
-      const float m1 = s_m[tid], l1 = s_l[tid], m2 = s_m[tid + w], l2 = s_l[tid + w];
-      const float mm = fmaxf(m1, m2);
-      float ll = 0.f;
-      if (mm != -INFINITY) {
-        ll = (m1 == -INFINITY ? 0.f : l1 * fast_exp2(m1 - mm)) + (m2 == -INFINITY ? 0.f : l2 * fast_exp2(m2 - mm));
-      }
-      s_m[tid] = mm; s_l[tid] = ll;
-    }
-    __syncthreads();
-  }
-  const float lse2 = s_m[0] + __log2f(s_l[0]);
-  const float lse = lse2 * kLn2;   // natural-log normaliser of S = z / tau
-  __syncthreads();
-
-  // 2. teacher distribution over the K ids
+  // 1. teacher distribution over the K ids
   const float inv_tau = 1.f / tau;
-  const float lse_a = teacher_row<256>(logit + (int64_t)t * K, K, inv_tau, s_a, s_m);
+  const float lse_a = teacher_row<256>(logit + (int64_t)t * K, K, inv_tau, s_a, s_red);
 
-  // 3. gathered student logits at the teacher ids
+  // 2. gathered student logits at the teacher ids
   const int lane = tid & 63, wid = tid >> 6;
   const u32x4* h = (const u32x4*)(hsrc + (int64_t)t * ldh);
-  for (int k = wid; k < K; k += 4) {
-    const int id = idx[(int64_t)t * K + k];
-    float dot = 0.f;
-    const bool ok = id >= 0 && id < V;
-    if (ok) {
-      const u32x4* w = (const u32x4*)(wsrc + (int64_t)id * ldw);
-      for (int u = lane; u < units16; u += 64) dot += dot16<E>(h[u], w[u]);
+  u32x4 hr[kMaxUnits];
+#pragma unroll
+  for (int r = 0; r < kMaxUnits; ++r) {
+    const int u = lane + 64 * r;
+    hr[r] = u < units16 ? h[u] : u32x4{0u, 0u, 0u, 0u};
+  }
+  const int32_t* idr = idx + (int64_t)t * K;
+  for (int k0 = wid * kGatherIds; k0 < K; k0 += 4 * kGatherIds) {
+    int id[kGatherIds];
+    bool ok[kGatherIds];
+    float dot[kGatherIds];
+#pragma unroll
+    for (int q = 0; q < kGatherIds; ++q) {
+      id[q] = k0 + q < K ? idr[k0 + q] : -1;
+      ok[q] = id[q] >= 0 && id[q] < V;
+      dot[q] = 0.f;
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    for (int r = 0; r < kMaxUnits; ++r) {
+      const int u = lane + 64 * r;
+      if (u < units16) {
+        u32x4 w[kGatherIds];
+#pragma unroll
+        for (int q = 0; q < kGatherIds; ++q)
+          w[q] = ok[q] ? ((const u32x4*)(wsrc + (int64_t)id[q] * ldw))[u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < kGatherIds; ++q) dot[q] += dot16<E>(hr[r], w[q]);
+      }
+    }
+    // rows longer than the register-held part (d_p * E > 12 KB)
+    for (int u = lane + 64 * kMaxUnits; u < units16; u += 64) {
+      const u32x4 hv = h[u];
+#pragma unroll
+      for (int q = 0; q < kGatherIds; ++q)
+        if (ok[q]) dot[q] += dot16<E>(hv, ((const u32x4*)(wsrc + (int64_t)id[q] * ldw))[u]);
+    }
+#pragma unroll
+    for (int q = 0; q < kGatherIds; ++q) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) dot[q] += __shfl_xor(dot[q], o);
+    }
     if (lane == 0) {
-      s_z[k] = ok ? dot : NAN;
-      if (!ok && status) *status = 7;  // KD_ERR_BAD_INDEX
+#pragma unroll
+      for (int q = 0; q < kGatherIds; ++q) {
+        if (k0 + q >= K) break;
+        s_z[k0 + q] = ok[q] ? dot[q] : NAN;
+        if (!ok[q] && status) *status = 7;   // KD_ERR_BAD_INDEX
+      }
     }
   }
   __syncthreads();
 
-  // 4. KL_t
+  // 3. KL_t
   double kl = 0.0;
   for (int k = tid; k < K; k += 256) {
     const float z = s_z[k];
@@ -407,8 +456,6 @@ __global__ __launch_bounds__(256) void kl_rows_kernel(
   kl = block_reduce<256>(kl, s_d, OpAddD());
   if (tid == 0) {
     rowkl[t] = kl;
-    lse2_out[t] = lse2;
-    if (row_lse) row_lse[t] = lse;
     if (row_kl) row_kl[t] = (float)kl;
   }
 }

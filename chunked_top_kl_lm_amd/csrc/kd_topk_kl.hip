@@ -33,20 +33,24 @@ namespace {
 
 // GEMM tile configurations (block tile BM x BN, WM x WN waves, STAGES LDS
 // stages of RB bytes of K), chosen by measurement on MI355X:
-//  - the logit GEMMs and the hidden-gradient GEMM: 256 x 256, 8 waves of
-//    128 x 64, 2 stages of 128 bytes (128 KB LDS, one block per CU; half the
-//    barriers of 64-byte stages);
-//  - the head-gradient GEMM, whose epilogue reads and writes the fp32 grad_W
-//    tile: 256 x 128, 8 waves of 64 x 64, 3 stages of 64 bytes (72 KB LDS,
-//    two blocks per CU, so one block's read-modify-write overlaps the other's
-//    MFMAs).
+//  - the logit GEMMs: 256 x 256, 8 waves of 128 x 64, 2 stages of 128 bytes
+//    (128 KB LDS, one block per CU; half the barriers of 64-byte stages);
+//  - the hidden-gradient GEMM (N = d): 256 x 256, or 256 x 320 (8 waves of
+//    64 x 160, 144 KB LDS) when that pads d less -- at d = 2880 the 320-wide
+//    tile covers d exactly where 256 wastes 6% of the columns;
+//  - the head-gradient GEMM (N = d, fp32 read-modify-write epilogue):
+//    256 x 192 (8 waves of 64 x 96, 112 KB LDS), or 256 x 128 when that pads
+//    d less.  Its epilogue keeps all grad_W loads of a wave in flight at once;
+//    with 256 x 256 tiles the registers allow only about an eighth of them.
 template <int BM_, int BN_, int WM_, int WN_, int ST_, int RB_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_, RB = RB_;
   static constexpr int kThreads = 64 * WM * WN;
 };
 using TileMain = TileCfg<256, 256, 2, 4, 2, 128>;
-using TileHead = TileCfg<256, 128, 4, 2, 3, 64>;
+using TileDhWide = TileCfg<256, 320, 4, 2, 2, 128>;
+using TileHead = TileCfg<256, 192, 4, 2, 2, 128>;
+using TileHeadNarrow = TileCfg<256, 128, 4, 2, 2, 128>;
 constexpr int kBM = TileMain::BM, kBN = TileMain::BN;
 constexpr int kWaveM = TileMain::BM / TileMain::WM;   // vocabulary strip of one LSE partial
 constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
@@ -60,6 +64,7 @@ struct Plan {
   int eb;             // element bytes
   bool pad_d;         // d is not a multiple of 64: use zero-padded copies
   int64_t d_p, V_p, R_p, Nd_p;
+  int dh_bn, dw_bn;   // column tile (over d) of the hidden- and head-gradient GEMMs
   int64_t nvt;        // LSE strips per row
   int splits;         // split-K factor of the hidden-gradient GEMM
   // workspace offsets
@@ -80,7 +85,9 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.d_p = round_up(d, 64);
   P.V_p = round_up(V, kBM);
   P.R_p = round_up(P.chunk, kBN);
-  P.Nd_p = round_up(d, kBN);
+  P.dh_bn = round_up(d, TileDhWide::BN) < round_up(d, TileMain::BN) ? TileDhWide::BN : TileMain::BN;
+  P.dw_bn = round_up(d, TileHead::BN) <= round_up(d, TileHeadNarrow::BN) ? TileHead::BN : TileHeadNarrow::BN;
+  P.Nd_p = round_up(d, P.dh_bn);
   P.nvt = P.V_p / kWaveM;
   // Addressing limits: per-tile buffer ranges and int32 tile indices.
   if (P.V_p > (1ll << 24) || P.d_p > (1ll << 20) || P.R_p > (1ll << 20) || T > (1ll << 31) / 2)
@@ -91,7 +98,7 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   // split count whose grid fills whole waves of 256 CUs best, with at least
   // two waves when the K extent allows, and a small penalty per split for
   // the partial-sum traffic.
-  const int64_t tiles = cdiv(P.R_p, kBM) * cdiv(P.Nd_p, kBN);
+  const int64_t tiles = cdiv(P.R_p, kBM) * (P.Nd_p / P.dh_bn);
   const int64_t k_tiles = P.V_p * P.eb / TileMain::RB;
   int best = 1;
   double best_cost = 1e30;
@@ -238,9 +245,12 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     }
     mark(slot + 1, 1);
     mark(slot + 2, 0);
-    hipLaunchKernelGGL(kl_rows_kernel<E>, dim3(R), dim3(256), 0, st, (const float2*)part, (int)P.R_p, (int)P.nvt,
-                       Hsrc, ldh, Wsrc, ldw, (int)(P.d_p * P.eb / 16), idx_c, logit_c, (int)K, (int)V, tau, lse2,
-                       rowkl, row_lse ? row_lse + c0 : nullptr, row_kl ? row_kl + c0 : nullptr, status);
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)cdiv(R, 32)), dim3(256), 0, st, (const float2*)part,
+                       (int)P.R_p, (int)P.nvt, R, lse2, row_lse ? row_lse + c0 : nullptr);
+    KD_LAUNCH_CHECK();
+    hipLaunchKernelGGL(kl_rows_kernel<E>, dim3(R), dim3(256), 0, st, (const float*)lse2, Hsrc, ldh, Wsrc, ldw,
+                       (int)(P.d_p * P.eb / 16), idx_c, logit_c, (int)K, (int)V, tau, rowkl,
+                       row_kl ? row_kl + c0 : nullptr, status);
     KD_LAUNCH_CHECK();
     hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(256), 0, st, (const double*)rowkl, mask_c, R, loss_acc);
     KD_LAUNCH_CHECK();
@@ -261,9 +271,15 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     mark(slot + 5, 0);
     // dH_c = G W  (A = G [Rt x V_p], B = W^T [d x V_p]), split-K over V
     {
-      GemmShape g = make_shape<TileMain>(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits, 8);
       EpiStoreSplit epi{dhp, P.Nd_p, P.R_p * P.Nd_p};
-      if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      GemmShape g;
+      if (P.dh_bn == TileDhWide::BN) {
+        g = make_shape<TileDhWide>(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits, 8);
+        if (launch_gemm<TileDhWide, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      } else {
+        g = make_shape<TileMain>(G, P.V_p, R, Wt, P.V_p, (int)d, P.V_p * P.eb, P.splits, 8);
+        if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      }
       mark(slot + 5, 1);
       mark(slot + 6, 0);
       const int64_t n = (int64_t)R * d;
@@ -275,9 +291,14 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     mark(slot + 7, 0);
     // dW (+)= G^T H_c  (A = G^T [V_p x R_p], B = H_c^T [d x R_p])
     {
-      GemmShape g = make_shape<TileHead>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
       EpiAccum epi{grad_W, d, (int)V, (int)d, c == 0 ? 1 : 0};
-      if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      if (P.dw_bn == TileHead::BN) {
+        GemmShape g = make_shape<TileHead>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
+        if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      } else {
+        GemmShape g = make_shape<TileHeadNarrow>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
+        if (launch_gemm<TileHeadNarrow, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      }
     }
     mark(slot + 7, 1);
   }

@@ -86,6 +86,8 @@ def _small(T, d, V, K, dtype, seed, tau=1.0, masked=(), dup_row=None, mask_none=
     (5, 64, 40, 40, 1.0),     # K = V (every id)
     (1, 128, 1000, 10, 0.5),  # one row
     (300, 192, 1000, 8, 1.3), # ragged vocabulary tile and chunk
+    (70, 576, 3000, 12, 1.0), # 320-wide hidden-gradient tile, ragged in d
+    (90, 704, 2500, 16, 0.8), # 192-wide head-gradient tile, ragged in d
 ])
 def test_edge_shapes(dtype, shape):
     T, d, V, K, tau = shape
