@@ -44,15 +44,47 @@ __device__ __forceinline__ void clamp_padding_rows(f32x16 (&acc)[FM][FN], int ro
 // never written (the chunk is "folded into the running loss and discarded":
 // Glonce, "Multiverse Computing cuts LLM distillation VRAM by 15x with
 // chunked KL loss", paragraph on Multiverse's two-part fix).
+//
+// The same epilogue also picks out the logits at the teacher's cached ids:
+// every (t, k) of the chunk is filed beforehand (build_hits) under the wave
+// sub-tile that holds z[t, idx[t,k]], and the wave copies those values from
+// its accumulators to zsel[t*K + k].  The top-K gather of the KL thus reads
+// no W rows.
+constexpr int kHitV = 128;   // vocabulary rows of one forward-GEMM wave tile
+constexpr int kHitT = 64;    // chunk rows of one forward-GEMM wave tile
+
 struct EpiLsePartial {
   float2* part;   // [nvt][ldp]: (max x2, sum exp2(x2 - max)) per strip and row
   int ldp;
   int V;
   float c2;       // log2(e) / tau
+  const int* hit_off;   // [nvt * nbt + 1] start of each wave tile's hit list
+  const uint2* hits;    // (slot t*K + k, (v % kHitV) << 6 | (t % kHitT))
+  float* zsel;          // [R * K] z at the teacher ids
+  int nbt;              // row groups of kHitT in the chunk
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
     const int vt = c.m0 / (FM * 32);
+    {
+      const int b = vt * nbt + c.n0 / kHitT;
+      const int e1 = hit_off[b + 1];
+      for (int e = hit_off[b]; e < e1; ++e) {
+        const uint2 h = hits[e];
+        const int vl = (int)(h.y >> 6), tl = (int)(h.y & 63);
+        const int rr = vl & 31;
+        const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
+        const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (i == (vl >> 5) && j == (tl >> 5)) z = acc[i][j][r];
+        if (c.lane == owner) zsel[h.x] = z;
+      }
+    }
     const int rows_valid = V - c.m0;          // vocabulary rows of this strip that exist
     if (rows_valid <= 0) {                    // strip entirely in the padding
 #pragma unroll
@@ -275,6 +307,96 @@ __global__ __launch_bounds__(1024) void prep_kernel(const uint8_t* mask, int64_t
   }
 }
 
+// Teacher-id hit lists of a chunk, filed by forward-GEMM wave tile
+// (vocabulary strip id / kHitV, row group t / kHitT): a counting sort in
+// three launches -- count, scan (which also clears the counts for the next
+// chunk), fill.  Entries of one list come in any order; each names its own
+// output slot, so the results do not depend on it.
+__global__ __launch_bounds__(256) void fill_i32_kernel(int* p, int64_t n, int v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void hit_count_kernel(const int32_t* idx, int R, int K, int V, int nbt,
+                                                        int* cnt) {
+  const int64_t n = (int64_t)R * K;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int id = idx[i];
+    if (id < 0 || id >= V) continue;
+    const int t = (int)(i / K);
+    atomicAdd(&cnt[(id / kHitV) * nbt + t / kHitT], 1);
+  }
+}
+
+// Exclusive scan of the counts into off (and cur, the fill cursors); the
+// counts are cleared for the next chunk.  One block; each pass covers
+// kScanTile counts, 16 contiguous per thread (vector loads, serial scan in
+// registers, wave scan with shuffles, wave totals through LDS).  The arrays
+// are padded to a multiple of kScanTile; padding counts stay zero.
+constexpr int kScanPer = 16;
+constexpr int kScanTile = 1024 * kScanPer;
+
+__global__ __launch_bounds__(1024) void hit_scan_kernel(int* cnt, int nb_p, int* off, int* cur, int nb) {
+  __shared__ int s_w[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < nb_p; base += kScanTile) {
+    int4* pc = (int4*)(cnt + base + tid * kScanPer);
+    int x[kScanPer];
+#pragma unroll
+    for (int q = 0; q < kScanPer / 4; ++q) {
+      const int4 v = pc[q];
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < kScanPer; ++q) {   // exclusive within the thread
+      const int c = x[q];
+      x[q] = tsum;
+      tsum += c;
+    }
+    int incl = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_w[w] = incl;
+    __syncthreads();
+    int wpre = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sw = s_w[i];
+      wpre += i < w ? sw : 0;
+      total += sw;
+    }
+    const int ex = carry + wpre + incl - tsum;
+    int4* po = (int4*)(off + base + tid * kScanPer);
+    int4* pu = (int4*)(cur + base + tid * kScanPer);
+#pragma unroll
+    for (int q = 0; q < kScanPer / 4; ++q) {
+      const int4 v = make_int4(ex + x[4 * q], ex + x[4 * q + 1], ex + x[4 * q + 2], ex + x[4 * q + 3]);
+      po[q] = v;
+      pu[q] = v;
+      pc[q] = make_int4(0, 0, 0, 0);
+    }
+    carry += total;
+    __syncthreads();                          // s_w is reused by the next pass
+  }
+  if (tid == 0) off[nb] = carry;
+}
+
+__global__ __launch_bounds__(256) void hit_fill_kernel(const int32_t* idx, int R, int K, int V, int nbt, int* cur,
+                                                       uint2* hits) {
+  const int64_t n = (int64_t)R * K;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int id = idx[i];
+    if (id < 0 || id >= V) continue;
+    const int t = (int)(i / K);
+    const int p = atomicAdd(&cur[(id / kHitV) * nbt + t / kHitT], 1);
+    hits[p] = make_uint2((uint32_t)i, (uint32_t)(((id % kHitV) << 6) | (t % kHitT)));
+  }
+}
+
 // dst[c][r] = src[r][c] for r < rows, c < cols; zero elsewhere in the
 // [dst_rows x ld_dst] destination.  64x64 tiles through LDS.
 template <class E>
@@ -311,24 +433,30 @@ __global__ __launch_bounds__(256) void pad_kernel(const typename E::T* src, int6
 }
 
 
-// Online logsumexp across vocabulary strips: for each chunk row t, merge the
-// per-strip (max, sum exp2) partials into the row's normaliser
-// lse2[t] = log2 sum_v exp2(z[t,v] log2(e) / tau).  Block = 32 rows x 8
-// strip slices; consecutive threads read consecutive rows of one strip
-// (coalesced); the 8 slices are merged in a fixed order.
-__global__ __launch_bounds__(256) void lse_merge_kernel(const float2* part, int ldp, int nvt, int R, float* lse2_out,
-                                                        float* row_lse) {
+// Online logsumexp across vocabulary strips, first level: for each chunk row
+// t and group of kMergeStrips strips, merge the per-strip (max, sum exp2)
+// partials into one.  Block = 32 rows x 8 strip slices; consecutive threads
+// read consecutive rows of one strip (coalesced); fixed merge order.  The
+// second level (over the groups) is done by kl_rows_kernel.
+constexpr int kMergeStrips = 64;
+
+__device__ __forceinline__ void lse_combine(float& M, float& L, float m2, float l2) {
+  if (l2 <= 0.f) return;                      // empty: strip with no vocabulary rows
+  if (m2 > M) { L = L * fast_exp2(M - m2) + l2; M = m2; }
+  else L += l2 * fast_exp2(m2 - M);
+}
+
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float2* part, int ldp, int nvt, int R, float2* part2) {
   __shared__ float s_m[8][32];
   __shared__ float s_l[8][32];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int t = blockIdx.x * 32 + tx;
+  const int v0 = blockIdx.y * kMergeStrips, v1 = min(nvt, v0 + kMergeStrips);
   float M = -INFINITY, L = 0.f;
   if (t < R) {
-    for (int vt = ty; vt < nvt; vt += 8) {
+    for (int vt = v0 + ty; vt < v1; vt += 8) {
       const float2 p = part[(int64_t)vt * ldp + t];
-      if (p.y <= 0.f) continue;               // strip with no vocabulary rows
-      if (p.x > M) { L = L * fast_exp2(M - p.x) + p.y; M = p.x; }
-      else L += p.y * fast_exp2(p.x - M);
+      lse_combine(M, L, p.x, p.y);
     }
   }
   s_m[ty][tx] = M;
@@ -336,119 +464,51 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float2* part, int 
   __syncthreads();
   if (ty == 0 && t < R) {
 #pragma unroll
-    for (int q = 1; q < 8; ++q) {
-      const float m2 = s_m[q][tx], l2 = s_l[q][tx];
-      if (l2 <= 0.f) continue;
-      if (m2 > M) { L = L * fast_exp2(M - m2) + l2; M = m2; }
-      else L += l2 * fast_exp2(m2 - M);
-    }
-    const float lse2 = M + __log2f(L);
-    lse2_out[t] = lse2;
-    if (row_lse) row_lse[t] = lse2 * kLn2;    // natural-log normaliser of S = z / tau
+    for (int q = 1; q < 8; ++q) lse_combine(M, L, s_m[q][tx], s_l[q][tx]);
+    part2[(int64_t)blockIdx.y * ldp + t] = make_float2(M, L);
   }
-}
-
-template <class E> __device__ __forceinline__ float dot16(u32x4 a, u32x4 b);
-template <> __device__ __forceinline__ float dot16<Bf16>(u32x4 a, u32x4 b) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16);
-    s += __uint_as_float(a[i] & 0xffff0000u) * __uint_as_float(b[i] & 0xffff0000u);
-  }
-  return s;
-}
-template <> __device__ __forceinline__ float dot16<F32>(u32x4 a, u32x4 b) {
-  f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
-  return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
 }
 
 // One block per chunk row t:
-//  1. the teacher's distribution p over its K cached ids;
-//  2. the student logits at those ids, z_k = h_t . W[idx_k] (gathered W
-//     rows; each wave takes four ids at a time so that four rows' loads are
-//     in flight; the hidden row is held in registers);
-//  3. KL_t = sum_k p_k (log p_k - (z_k / tau - LSE_t)).
+//  1. the row's normaliser LSE_t from the ng group partials of lse_merge_kernel
+//     (second level of the online logsumexp), written to lse2 / row_lse;
+//  2. the teacher's distribution p over its K cached ids;
+//  3. KL_t = sum_k p_k (log p_k - (z_k / tau - LSE_t)), with z_k the student
+//     logit at id k captured by the forward epilogue.
 // Invalid ids set *status and contribute nothing.
-constexpr int kGatherIds = 4;     // ids per wave per step
-constexpr int kMaxUnits = 12;     // 16-byte units of the hidden row held per lane (the first 12 KB)
-
-template <class E>
-__global__ __launch_bounds__(256) void kl_rows_kernel(
-    const float* lse2_in, const typename E::T* hsrc, int64_t ldh, const typename E::T* wsrc, int64_t ldw,
-    int units16, const int32_t* idx, const float* logit, int K, int V, float tau, double* rowkl, float* row_kl,
-    int32_t* status) {
+__global__ __launch_bounds__(256) void kl_rows_kernel(const float2* part2, int ldp, int ng, float* lse2_out,
+                                                      float* row_lse, const float* zsel, const int32_t* idx,
+                                                      const float* logit, int K, int V, float tau, double* rowkl,
+                                                      float* row_kl, int32_t* status) {
   __shared__ float s_a[kMaxK];
-  __shared__ float s_z[kMaxK];
   __shared__ float s_red[256];
   __shared__ double s_d[256];
   const int t = blockIdx.x, tid = threadIdx.x;
-  const float lse = lse2_in[t] * kLn2;        // natural-log normaliser of S = z / tau
 
-  // 1. teacher distribution over the K ids
+  // 1. LSE_t
+  float M = -INFINITY, L = 0.f;
+  for (int g = tid; g < ng; g += 256) {
+    const float2 p = part2[(int64_t)g * ldp + t];
+    lse_combine(M, L, p.x, p.y);
+  }
+  const float Mx = block_reduce<256>(M, s_red, OpMax());
+  const float Ls = block_reduce<256>(L > 0.f ? L * fast_exp2(M - Mx) : 0.f, s_red, OpAddF());
+  const float lse2 = Mx + __log2f(Ls);
+  if (tid == 0) {
+    lse2_out[t] = lse2;
+    if (row_lse) row_lse[t] = lse2 * kLn2;
+  }
+  const float lse = lse2 * kLn2;              // natural-log normaliser of S = z / tau
   const float inv_tau = 1.f / tau;
   const float lse_a = teacher_row<256>(logit + (int64_t)t * K, K, inv_tau, s_a, s_red);
-
-  // 2. gathered student logits at the teacher ids
-  const int lane = tid & 63, wid = tid >> 6;
-  const u32x4* h = (const u32x4*)(hsrc + (int64_t)t * ldh);
-  u32x4 hr[kMaxUnits];
-#pragma unroll
-  for (int r = 0; r < kMaxUnits; ++r) {
-    const int u = lane + 64 * r;
-    hr[r] = u < units16 ? h[u] : u32x4{0u, 0u, 0u, 0u};
-  }
-  const int32_t* idr = idx + (int64_t)t * K;
-  for (int k0 = wid * kGatherIds; k0 < K; k0 += 4 * kGatherIds) {
-    int id[kGatherIds];
-    bool ok[kGatherIds];
-    float dot[kGatherIds];
-#pragma unroll
-    for (int q = 0; q < kGatherIds; ++q) {
-      id[q] = k0 + q < K ? idr[k0 + q] : -1;
-      ok[q] = id[q] >= 0 && id[q] < V;
-      dot[q] = 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < kMaxUnits; ++r) {
-      const int u = lane + 64 * r;
-      if (u < units16) {
-        u32x4 w[kGatherIds];
-#pragma unroll
-        for (int q = 0; q < kGatherIds; ++q)
-          w[q] = ok[q] ? ((const u32x4*)(wsrc + (int64_t)id[q] * ldw))[u] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int q = 0; q < kGatherIds; ++q) dot[q] += dot16<E>(hr[r], w[q]);
-      }
-    }
-    // rows longer than the register-held part (d_p * E > 12 KB)
-    for (int u = lane + 64 * kMaxUnits; u < units16; u += 64) {
-      const u32x4 hv = h[u];
-#pragma unroll
-      for (int q = 0; q < kGatherIds; ++q)
-        if (ok[q]) dot[q] += dot16<E>(hv, ((const u32x4*)(wsrc + (int64_t)id[q] * ldw))[u]);
-    }
-#pragma unroll
-    for (int q = 0; q < kGatherIds; ++q) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) dot[q] += __shfl_xor(dot[q], o);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int q = 0; q < kGatherIds; ++q) {
-        if (k0 + q >= K) break;
-        s_z[k0 + q] = ok[q] ? dot[q] : NAN;
-        if (!ok[q] && status) *status = 7;   // KD_ERR_BAD_INDEX
-      }
-    }
-  }
-  __syncthreads();
-
-  // 3. KL_t
   double kl = 0.0;
   for (int k = tid; k < K; k += 256) {
-    const float z = s_z[k];
-    if (z != z) continue;                     // invalid id: no contribution
+    const int id = idx[(int64_t)t * K + k];
+    if (id < 0 || id >= V) {
+      if (status) *status = 7;                // KD_ERR_BAD_INDEX
+      continue;
+    }
+    const float z = zsel[(int64_t)t * K + k];
     const float logp = s_a[k] - lse_a;
     const float p = expf(logp);
     if (p > 0.f) kl += (double)p * ((double)logp - ((double)z * inv_tau - (double)lse));

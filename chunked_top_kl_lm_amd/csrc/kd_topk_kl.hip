@@ -10,10 +10,10 @@
 //   in the backward pass -- Glonce, "Multiverse Computing cuts LLM
 //   distillation VRAM by 15x with chunked KL loss", paragraph on Multiverse's
 //   two-part fix):
-//     transpose H_c   H_c^T for the head-gradient GEMM
-//     GEMM + LSE      z^T = W H_c^T, per-strip (max, sum exp) partials
-//     KL rows         online merge -> LSE_t; teacher p; gathered z at the ids;
-//                     KL_t
+//     transpose H_c   H_c^T for the head-gradient GEMM; teacher-id hit lists
+//     GEMM + LSE      z^T = W H_c^T, per-strip (max, sum exp) partials, and
+//                     z at the teacher ids picked from the accumulators
+//     KL rows         online merge -> LSE_t; teacher p; KL_t
 //     chunk loss      fixed-order fp64 sum of m_t KL_t
 //     GEMM + grad     recompute z^T, G = (tau/N) m q in two layouts
 //     scatter         G[t, id] -= (tau/N) m_t P[t, id]
@@ -68,7 +68,11 @@ struct Plan {
   int64_t nvt;        // LSE strips per row
   int splits;         // split-K factor of the hidden-gradient GEMM
   // workspace offsets
+  int64_t nbt, nhb;   // teacher-id hit lists: row groups per chunk, lists per chunk
+  int64_t nhb_p;      // nhb padded for the scan
+  int64_t ng;         // first-level LSE merge groups per row
   size_t off_scalar, off_wt, off_wp, off_hp, off_ht, off_g, off_gt, off_part, off_lse2, off_rowkl, off_dh;
+  size_t off_hcnt, off_hoff, off_hcur, off_hits, off_zsel, off_part2;
   size_t total;
 };
 
@@ -89,15 +93,20 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.dw_bn = round_up(d, TileHead::BN) <= round_up(d, TileHeadNarrow::BN) ? TileHead::BN : TileHeadNarrow::BN;
   P.Nd_p = round_up(d, P.dh_bn);
   P.nvt = P.V_p / kWaveM;
+  P.nbt = P.R_p / kHitT;
+  P.nhb = P.nvt * P.nbt;
+  P.nhb_p = round_up(P.nhb, kScanTile);
+  P.ng = cdiv(P.nvt, kMergeStrips);
   // Addressing limits: per-tile buffer ranges and int32 tile indices.
   if (P.V_p > (1ll << 24) || P.d_p > (1ll << 20) || P.R_p > (1ll << 20) || T > (1ll << 31) / 2)
     return KD_ERR_BAD_SHAPE;
   if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_p * P.eb >= (1ll << 32))
     return KD_ERR_BAD_SHAPE;
+  // hit-list entries are int32-indexed
+  if (P.R_p * K >= (1ll << 31) || P.nhb_p >= (1ll << 28)) return KD_ERR_BAD_SHAPE;
   // split-K of the hidden-gradient GEMM (output only chunk x d): pick the
   // split count whose grid fills whole waves of 256 CUs best, with at least
-  // two waves when the K extent allows, and a small penalty per split for
-  // the partial-sum traffic.
+  // one full wave, and a small penalty per split for the partial-sum traffic.
   const int64_t tiles = cdiv(P.R_p, kBM) * (P.Nd_p / P.dh_bn);
   const int64_t k_tiles = P.V_p * P.eb / TileMain::RB;
   int best = 1;
@@ -106,7 +115,7 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
     const int64_t blocks = tiles * sp;
     const double waves = (double)blocks / kNumCU;
     double cost = (double)cdiv(blocks, kNumCU) / waves + 0.004 * sp;
-    if (blocks < 2 * kNumCU) cost += 1.0;                  // too little parallelism
+    if (blocks < kNumCU) cost += 1.0;                      // too little parallelism
     if (k_tiles / sp < 16) cost += 1.0;                     // splits too thin
     if (cost < best_cost) { best_cost = cost; best = sp; }
   }
@@ -127,6 +136,12 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.off_lse2 = o; o = align256(o + (size_t)P.R_p * sizeof(float));
   P.off_rowkl = o; o = align256(o + (size_t)P.R_p * sizeof(double));
   P.off_dh = o; o = align256(o + (size_t)P.splits * P.R_p * P.Nd_p * sizeof(float));
+  P.off_hcnt = o; o = align256(o + (size_t)P.nhb_p * sizeof(int));
+  P.off_hoff = o; o = align256(o + (size_t)(P.nhb_p + 1) * sizeof(int));
+  P.off_hcur = o; o = align256(o + (size_t)P.nhb_p * sizeof(int));
+  P.off_hits = o; o = align256(o + (size_t)P.R_p * K * sizeof(uint2));
+  P.off_zsel = o; o = align256(o + (size_t)P.R_p * K * sizeof(float));
+  P.off_part2 = o; o = align256(o + (size_t)P.ng * P.R_p * sizeof(float2));
   P.total = o;
   return KD_OK;
 }
@@ -185,12 +200,21 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
   float* lse2 = (float*)(ws + P.off_lse2);
   double* rowkl = (double*)(ws + P.off_rowkl);
   float* dhp = (float*)(ws + P.off_dh);
+  int* hcnt = (int*)(ws + P.off_hcnt);
+  int* hoff = (int*)(ws + P.off_hoff);
+  int* hcur = (int*)(ws + P.off_hcur);
+  uint2* hits = (uint2*)(ws + P.off_hits);
+  float* zsel = (float*)(ws + P.off_zsel);
+  float2* part2 = (float2*)(ws + P.off_part2);
 
   const int64_t T_ = P.T, d = P.d, V = P.V, K = P.K;
   const float c2 = kLog2e / tau;
 
   mark(pro_slot, 0);
   hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, st, mask, T_, count, loss_acc, status);
+  KD_LAUNCH_CHECK();
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(P.nhb_p, 256), 4096)), dim3(256), 0, st,
+                     hcnt, P.nhb_p, 0);
   KD_LAUNCH_CHECK();
   // W^T, zero-padded to [d_p][V_p]
   hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.V_p / 64), (unsigned)(P.d_p / 64)), dim3(256), 0,
@@ -230,27 +254,38 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.R_p / 64), (unsigned)(P.d_p / 64)), dim3(256), 0,
                        st, Hc, d, (int64_t)R, d, Ht, P.R_p);
     KD_LAUNCH_CHECK();
-    mark(slot + 0, 1);
-
     const uint8_t* mask_c = mask ? mask + c0 : nullptr;
     const int32_t* idx_c = idx + c0 * K;
     const float* logit_c = logit + c0 * K;
+    // teacher-id hit lists for the forward epilogue
+    {
+      const unsigned nblk = (unsigned)std::min<int64_t>(cdiv((int64_t)R * K, 256), 4096);
+      hipLaunchKernelGGL(hit_count_kernel, dim3(nblk), dim3(256), 0, st, idx_c, R, (int)K, (int)V, (int)P.nbt, hcnt);
+      KD_LAUNCH_CHECK();
+      hipLaunchKernelGGL(hit_scan_kernel, dim3(1), dim3(1024), 0, st, hcnt, (int)P.nhb_p, hoff, hcur, (int)P.nhb);
+      KD_LAUNCH_CHECK();
+      hipLaunchKernelGGL(hit_fill_kernel, dim3(nblk), dim3(256), 0, st, idx_c, R, (int)K, (int)V, (int)P.nbt, hcur,
+                         hits);
+      KD_LAUNCH_CHECK();
+    }
+    mark(slot + 0, 1);
+
 
     // forward: z^T = W H_c^T -> LSE partials
     mark(slot + 1, 0);
     {
       GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-      EpiLsePartial epi{part, (int)P.R_p, (int)V, c2};
+      EpiLsePartial epi{part, (int)P.R_p, (int)V, c2, hoff, hits, zsel, (int)P.nbt};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 1, 1);
     mark(slot + 2, 0);
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)cdiv(R, 32)), dim3(256), 0, st, (const float2*)part,
-                       (int)P.R_p, (int)P.nvt, R, lse2, row_lse ? row_lse + c0 : nullptr);
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)cdiv(R, 32), (unsigned)P.ng), dim3(256), 0, st,
+                       (const float2*)part, (int)P.R_p, (int)P.nvt, R, part2);
     KD_LAUNCH_CHECK();
-    hipLaunchKernelGGL(kl_rows_kernel<E>, dim3(R), dim3(256), 0, st, (const float*)lse2, Hsrc, ldh, Wsrc, ldw,
-                       (int)(P.d_p * P.eb / 16), idx_c, logit_c, (int)K, (int)V, tau, rowkl,
-                       row_kl ? row_kl + c0 : nullptr, status);
+    hipLaunchKernelGGL(kl_rows_kernel, dim3(R), dim3(256), 0, st, (const float2*)part2, (int)P.R_p, (int)P.ng, lse2,
+                       row_lse ? row_lse + c0 : nullptr, (const float*)zsel, idx_c, logit_c, (int)K, (int)V, tau,
+                       rowkl, row_kl ? row_kl + c0 : nullptr, status);
     KD_LAUNCH_CHECK();
     hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(256), 0, st, (const double*)rowkl, mask_c, R, loss_acc);
     KD_LAUNCH_CHECK();

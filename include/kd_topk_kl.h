@@ -127,10 +127,12 @@ int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype,
  * nchunks = ceil(T / min(chunk, T)).  The call records events[2*i] before and
  * events[2*i + 1] after the launches of
  *   i = c * KD_NUM_PHASES + p   phase p of chunk c:
- *       0 zero-padded H_c and H_c^T, 1 forward GEMM with the logsumexp
- *       partials, 2 KL rows and the chunk's loss sum, 3 recompute GEMM with
- *       the gradient epilogue, 4 sparse teacher scatter, 5 hidden-gradient
- *       GEMM, 6 its split-K reduction, 7 head-gradient GEMM;
+ *       0 zero-padded H_c and H_c^T and the teacher-id hit lists,
+ *       1 forward GEMM with the logsumexp partials and the logits at the
+ *       teacher ids, 2 logsumexp merge, KL rows and the chunk's loss sum,
+ *       3 recompute GEMM with the gradient epilogue, 4 sparse teacher
+ *       scatter, 5 hidden-gradient GEMM, 6 its split-K reduction,
+ *       7 head-gradient GEMM;
  *   i = KD_NUM_PHASES * nchunks      the prologue (count N, W^T);
  *   i = KD_NUM_PHASES * nchunks + 1  the final loss.
  * Everything else is as for kd_topk_kl_fwd_bwd; KD_ERR_NULL_ARG if events is
