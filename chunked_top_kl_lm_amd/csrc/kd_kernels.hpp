@@ -228,6 +228,22 @@ struct EpiAccum {
         }
       return;
     }
+    // ragged edge: the old values are loaded unconditionally from clamped
+    // (in-bounds) addresses, so the loads stay in flight together; only the
+    // stores are predicated
+    if (!first) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int nc = min(c.n0 + 32 * j + acc_col(c.lane), N - 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int mc = min(c.m0 + 32 * i + acc_row(r, c.lane), M - 1);
+            acc[i][j][r] += out[(int64_t)mc * ld + nc];
+          }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -237,10 +253,7 @@ struct EpiAccum {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = c.m0 + 32 * i + acc_row(r, c.lane);
-          if (m < M) {
-            float* p = out + (int64_t)m * ld + n;
-            *p = first ? acc[i][j][r] : *p + acc[i][j][r];
-          }
+          if (m < M) out[(int64_t)m * ld + n] = acc[i][j][r];
         }
       }
   }
