@@ -31,6 +31,10 @@ PEAK_HBM_GBS = 8000.0
 GEMM_PHASES = ("gemm_fwd_lse", "gemm_bwd_grad", "gemm_dhidden", "gemm_dW")
 KERNEL_SOURCES = ("chunked_top_kl_lm_amd/csrc/kd_gemm.hpp", "chunked_top_kl_lm_amd/csrc/kd_kernels.hpp",
                   "chunked_top_kl_lm_amd/csrc/kd_topk_kl.hip")
+# epilogue type in each GEMM phase's kernel name (rocprofv3 reports kernel names)
+PHASE_KERNEL_TAGS = {"gemm_fwd_lse": "EpiLsePartial", "gemm_bwd_grad": "EpiGrad",
+                     "gemm_dhidden": "EpiStoreSplit", "gemm_dW": "EpiAccum"}
+COPY_PROBE_BYTES = 2 ** 31     # --copy-probe: one device copy of 2 GiB (read 2 GiB, write 2 GiB)
 
 
 def kernel_source_hash() -> str:
@@ -74,23 +78,64 @@ def cpu_baseline(x: dict, target_s: float) -> dict:
             "seconds": t, "rows": n}
 
 
-def load_traffic(kernel: str, per_launch_units: int) -> dict | None:
-    """HBM traffic of the dominant kernel from the committed PMC summary, if it
-    was taken on the current kernel sources."""
+def load_traffic(kernel: str):
+    """HBM bytes per launch of a GEMM phase's kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy
+    calibration), if it was taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(p):
-        return None
+        return None, None
     try:
         rec = json.load(open(p))
     except Exception:
-        return None
+        return None, None
     if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
+        return None, None
     k = rec.get("kernels", {}).get(kernel)
     if not k:
-        return None
-    return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
-            "bytes": k["fetch_bytes"] + k["write_bytes"], "scale": rec.get("copy_scale")}
+        return None, None
+    return k["fetch_bytes"] + k["write_bytes"], {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+                                                 "copy_scale": rec.get("copy_scale")}
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
+    """Turn two rocprofv3 --pmc runs of `bench.py --steps 1 --warmup 0
+    --copy-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into
+    profiles/pmc_traffic.json: per GEMM phase, the mean bytes per launch, each
+    counter scaled so that the 2 GiB probe copy reads and writes 2 GiB."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        by = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                by[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+        return by
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_f = max(max(v) for k, v in fetch.items() if "copyBuffer" in k)
+    copy_w = max(max(v) for k, v in write.items() if "copyBuffer" in k)
+    scale = {"fetch": COPY_PROBE_BYTES / copy_f, "write": COPY_PROBE_BYTES / copy_w}
+    kernels = {}
+    for phase, tag in PHASE_KERNEL_TAGS.items():
+        f = [x for k, v in fetch.items() if tag in k and "kd::" in k for x in v]
+        w = [x for k, v in write.items() if tag in k and "kd::" in k for x in v]
+        kernels[phase] = {"fetch_bytes": scale["fetch"] * sum(f) / len(f),
+                          "write_bytes": scale["write"] * sum(w) / len(w), "dispatches": len(f),
+                          "fetch_raw_bytes": sum(f) / len(f), "write_raw_bytes": sum(w) / len(w)}
+    rec = {"kernel_source_hash": kernel_source_hash(), "copy_scale": scale,
+           "copy_raw_bytes": {"fetch": copy_f, "write": copy_w}, "kernels": kernels}
+    with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print("| phase | dispatches | fetch GB/launch | write GB/launch | raw fetch GB | raw write GB |")
+    print("|---|---|---|---|---|---|")
+    for phase, k in kernels.items():
+        print(f"| {phase} | {k['dispatches']} | {k['fetch_bytes'] / 1e9:.3f} | {k['write_bytes'] / 1e9:.3f} | "
+              f"{k['fetch_raw_bytes'] / 1e9:.3f} | {k['write_raw_bytes'] / 1e9:.3f} |")
+    print(f"\nCopy calibration (2 GiB copy): FETCH_SIZE read {copy_f / 2**30:.3f} GiB (scale {scale['fetch']:.3f}), "
+          f"WRITE_SIZE read {copy_w / 2**30:.3f} GiB (scale {scale['write']:.3f}).")
+    return 0
 
 
 def main() -> int:
@@ -106,11 +151,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 2 GiB device copy (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/pmc_traffic.json from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        return ingest_pmc(*args.ingest_pmc)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused chunked KL loss runs on a single MI355X "
-              "with no collectives; multi-GPU runs are not part of this build.", file=sys.stderr)
+              "with no collectives between GPUs; runs on more than one GPU are not supported.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -197,7 +246,7 @@ def main() -> int:
     # (average over launches; the last chunk may be ragged)
     alg_flops = 2.0 * d * V * T / nchunks
     achieved = alg_flops / (launch_ms * 1e-3) / 1e12
-    traffic = load_traffic(dom, eff_chunk)
+    traffic, traffic_detail = load_traffic(dom)
 
     if args.copy_probe:
         src = torch.empty(2**30 // 2, dtype=torch.float32, device=dev).fill_(1.0)
@@ -228,7 +277,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "launch_ms": launch_ms,
                      "alg_flops_per_launch": alg_flops,
-                     "traffic": traffic},
+                     "traffic": traffic, "traffic_detail": traffic_detail},
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "wall_s_timed": wall,
         "input_gen_s": t_gen,

@@ -11,6 +11,7 @@ import ctypes
 import os
 
 __all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
+           "fwd", "bwd", "fwd_workspace_bytes", "bwd_workspace_bytes", "KdTopKKLFunction", "kd_topk_kl_loss",
            "status_str", "STATUS"]
 
 KD_BF16 = 0
@@ -48,6 +49,16 @@ def lib() -> ctypes.CDLL:
         L.kd_topk_kl_fwd_bwd.restype = i32
         L.kd_topk_kl_fwd_bwd_timed.argtypes = L.kd_topk_kl_fwd_bwd.argtypes + [vp]
         L.kd_topk_kl_fwd_bwd_timed.restype = i32
+        L.kd_topk_kl_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+        L.kd_topk_kl_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.kd_topk_kl_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+        L.kd_topk_kl_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.kd_topk_kl_fwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, i64,
+                                     vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+        L.kd_topk_kl_fwd.restype = i32
+        L.kd_topk_kl_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, i64,
+                                     vp, vp, vp, i32, vp, i32, vp, vp, ctypes.c_size_t, vp, vp]
+        L.kd_topk_kl_bwd.restype = i32
         L.kd_status_str.argtypes = [i32]
         L.kd_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -62,8 +73,40 @@ def workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> i
     return int(lib().kd_topk_kl_workspace_bytes(T, d, V, K, chunk, dtype))
 
 
+def fwd_workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> int:
+    return int(lib().kd_topk_kl_fwd_workspace_bytes(T, d, V, K, chunk, dtype))
+
+
+def bwd_workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> int:
+    return int(lib().kd_topk_kl_bwd_workspace_bytes(T, d, V, K, chunk, dtype))
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_inputs(hidden, W, teacher_idx, teacher_logit, mask):
+    import torch
+    T, d = hidden.shape
+    V = W.shape[0]
+    K = teacher_idx.shape[1]
+    if hidden.dtype == torch.bfloat16:
+        dt = KD_BF16
+    elif hidden.dtype == torch.float32:
+        dt = KD_F32
+    else:
+        raise TypeError("hidden must be bfloat16 or float32")
+    for name, tns in (("hidden", hidden), ("W", W), ("teacher_idx", teacher_idx),
+                      ("teacher_logit", teacher_logit), ("mask", mask)):
+        if tns is not None and not tns.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if W.dtype != hidden.dtype or teacher_idx.dtype != torch.int32 or teacher_logit.dtype != torch.float32:
+        raise TypeError("W must match hidden's dtype; teacher_idx int32; teacher_logit float32")
+    if W.shape[1] != d or tuple(teacher_logit.shape) != (T, K) or teacher_idx.shape[0] != T:
+        raise ValueError("shapes: hidden [T,d], W [V,d], teacher_idx and teacher_logit [T,K]")
+    if mask is not None and (mask.dtype != torch.uint8 or tuple(mask.shape) != (T,)):
+        raise TypeError("mask must be uint8 [T]")
+    return T, d, V, K, dt
 
 
 def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
@@ -84,23 +127,7 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     """
     import torch
     L = lib()
-    T, d = hidden.shape
-    V = W.shape[0]
-    K = teacher_idx.shape[1]
-    if hidden.dtype == torch.bfloat16:
-        dt = KD_BF16
-    elif hidden.dtype == torch.float32:
-        dt = KD_F32
-    else:
-        raise TypeError("hidden must be bfloat16 or float32")
-    for name, tns in (("hidden", hidden), ("W", W), ("teacher_idx", teacher_idx),
-                      ("teacher_logit", teacher_logit), ("mask", mask)):
-        if tns is not None and not tns.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if W.dtype != hidden.dtype or teacher_idx.dtype != torch.int32 or teacher_logit.dtype != torch.float32:
-        raise TypeError("W must match hidden's dtype; teacher_idx int32; teacher_logit float32")
-    if mask is not None and mask.dtype != torch.uint8:
-        raise TypeError("mask must be uint8")
+    T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
     dev = hidden.device
     if out is None:
         loss = torch.empty((), dtype=torch.float32, device=dev)
@@ -131,3 +158,140 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     if row_stats:
         return loss, gH, gW, rl, rk
     return loss, gH, gW
+
+
+def fwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chunk: int = 2048,
+        row_kl: bool = False, workspace=None, status=None):
+    """Forward only (kd_topk_kl_fwd).  Returns (loss [0-d float32], row_lse
+    [T] float32) and, with row_kl, also the per-row KL [T].  row_lse is what
+    bwd() needs."""
+    import torch
+    T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
+    dev = hidden.device
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    rl = torch.empty(T, dtype=torch.float32, device=dev)
+    rk = torch.empty(T, dtype=torch.float32, device=dev) if row_kl else None
+    nbytes = fwd_workspace_bytes(T, d, V, K, chunk, dt)
+    if nbytes == 0:
+        raise KdError(2)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kd_topk_kl_fwd(_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit), _ptr(mask),
+                              T, d, V, K, float(tau), int(chunk), _ptr(loss), _ptr(rl), _ptr(rk),
+                              _ptr(workspace), workspace.numel(), _ptr(status), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KdError(rc)
+    return (loss, rl, rk) if row_kl else (loss, rl)
+
+
+def bwd(hidden, W, teacher_idx, teacher_logit, mask, row_lse, tau: float = 1.0, chunk: int = 2048,
+        grad_loss=None, grad_hidden="float32", grad_W=True, accumulate_into=None, grad_W_bf16: bool = False,
+        workspace=None, status=None):
+    """Backward only (kd_topk_kl_bwd): gradients of grad_loss * loss.
+
+    grad_loss: 0-d float32 CUDA tensor or None (= 1).  grad_hidden:
+    "float32", "bfloat16" or None (not computed).  grad_W: True (a new fp32
+    [V,d] tensor), False (not computed); accumulate_into: an fp32 [V,d] CUDA
+    tensor that the head gradient is added to instead (returned as grad_W).
+    grad_W_bf16: also return a bf16 copy of the final grad_W.  Returns
+    (grad_hidden, grad_W, grad_W_bf16), with None for what was not asked."""
+    import torch
+    T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
+    dev = hidden.device
+    if row_lse.dtype != torch.float32 or tuple(row_lse.shape) != (T,) or not row_lse.is_contiguous():
+        raise ValueError("row_lse must be a contiguous float32 [T] tensor")
+    if grad_loss is not None and (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1):
+        raise ValueError("grad_loss must be a one-element float32 tensor")
+    gh_dt = {"float32": (KD_F32, torch.float32), "bfloat16": (KD_BF16, torch.bfloat16), None: (KD_F32, None)}
+    if grad_hidden not in gh_dt:
+        raise ValueError("grad_hidden must be 'float32', 'bfloat16' or None")
+    gh_code, gh_torch = gh_dt[grad_hidden]
+    gH = torch.empty((T, d), dtype=gh_torch, device=dev) if gh_torch is not None else None
+    if accumulate_into is not None:
+        if accumulate_into.dtype != torch.float32 or tuple(accumulate_into.shape) != (V, d) \
+                or not accumulate_into.is_contiguous():
+            raise ValueError("accumulate_into must be a contiguous float32 [V,d] tensor")
+        gW, acc = accumulate_into, 1
+    else:
+        gW, acc = (torch.empty((V, d), dtype=torch.float32, device=dev) if grad_W else None), 0
+    gWb = torch.empty((V, d), dtype=torch.bfloat16, device=dev) if (grad_W_bf16 and gW is not None) else None
+    nbytes = bwd_workspace_bytes(T, d, V, K, chunk, dt)
+    if nbytes == 0:
+        raise KdError(2)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kd_topk_kl_bwd(_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit), _ptr(mask),
+                              T, d, V, K, float(tau), int(chunk), _ptr(row_lse), _ptr(grad_loss), _ptr(gH),
+                              gh_code, _ptr(gW), acc, _ptr(gWb), _ptr(workspace), workspace.numel(), _ptr(status),
+                              ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KdError(rc)
+    return gH, gW, gWb
+
+
+def _autograd_function():
+    import torch
+
+    class KdTopKKLFunction(torch.autograd.Function):
+        """The fused chunked top-K KL loss as an autograd node.
+
+        forward(hidden, W, teacher_idx, teacher_logit, mask, tau, chunk,
+        grad_W_accumulator) -> loss (0-d float32).  Only the per-row
+        logsumexp is saved besides the inputs; the backward recomputes each
+        chunk's logits.  The hidden gradient comes back in hidden's dtype.
+        The head gradient: with a grad_W_accumulator (fp32 [V,d], e.g. a
+        master-weight gradient buffer) it is added there in fp32 and W gets
+        no .grad; otherwise it is returned in W's dtype."""
+
+        @staticmethod
+        def forward(ctx, hidden, W, teacher_idx, teacher_logit, mask, tau, chunk, grad_W_accumulator):
+            loss, row_lse = fwd(hidden, W, teacher_idx, teacher_logit, mask, tau, chunk)
+            ctx.save_for_backward(hidden, W, teacher_idx, teacher_logit, mask, row_lse)
+            ctx.tau, ctx.chunk, ctx.acc = tau, chunk, grad_W_accumulator
+            return loss
+
+        @staticmethod
+        def backward(ctx, grad_loss):
+            hidden, W, teacher_idx, teacher_logit, mask, row_lse = ctx.saved_tensors
+            need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+            if not (need_h or need_w):
+                return (None,) * 8
+            g = grad_loss.reshape(()).to(torch.float32).contiguous()
+            gh_kind = ("bfloat16" if hidden.dtype == torch.bfloat16 else "float32") if need_h else None
+            use_acc = need_w and ctx.acc is not None
+            gH, gW, gWb = bwd(hidden, W, teacher_idx, teacher_logit, mask, row_lse, ctx.tau, ctx.chunk,
+                              grad_loss=g, grad_hidden=gh_kind, grad_W=need_w and not use_acc,
+                              accumulate_into=ctx.acc if use_acc else None,
+                              grad_W_bf16=need_w and not use_acc and W.dtype == torch.bfloat16)
+            if not need_w or use_acc:
+                dW = None
+            else:
+                dW = gWb if W.dtype == torch.bfloat16 else gW
+            return gH, dW, None, None, None, None, None, None
+
+    return KdTopKKLFunction
+
+
+_FN = None
+
+
+def __getattr__(name):
+    global _FN
+    if name == "KdTopKKLFunction":
+        if _FN is None:
+            _FN = _autograd_function()
+        return _FN
+    raise AttributeError(name)
+
+
+def kd_topk_kl_loss(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chunk: int = 2048,
+                    grad_W_accumulator=None):
+    """Differentiable loss: tau^2 * masked mean over positions of
+    KL(teacher top-K softmax || student full-vocabulary softmax), computed
+    and differentiated by the HIP library."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    return _FN.apply(hidden, W, teacher_idx, teacher_logit, mask, tau, chunk, grad_W_accumulator)

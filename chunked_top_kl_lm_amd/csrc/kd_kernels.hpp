@@ -113,25 +113,33 @@ struct EpiLsePartial {
 };
 
 // Backward recompute of a chunk: the logit gradient of the loss,
-// G[t,v] = (tau/N) m_t q[t,v], written in two layouts (G [R_p][V_p] and
-// G^T [V_p][R_p]) for the two gradient GEMMs; entries at v >= V are unused.  The sparse teacher part
-// -(tau/N) m_t P[t,v] is subtracted afterwards by scatter_sparse_kernel.
+// G[t,v] = g (tau/N) m_t q[t,v] (g = dL/dloss from the caller, 1 in the
+// fused call), written in two layouts (G [R_p][V_p] and G^T [V_p][R_p]) for
+// the two gradient GEMMs; entries at v >= V are unused.  The sparse teacher
+// part -g (tau/N) m_t P[t,v] is subtracted afterwards by
+// scatter_sparse_kernel.
+__device__ __forceinline__ float grad_scale(const int* count, const float* grad_loss, float tau) {
+  const int N = *count;
+  return N > 0 ? (grad_loss ? *grad_loss : 1.f) * (tau / (float)N) : 0.f;
+}
+
 template <class E>
 struct EpiGrad {
   typename E::T* G;
   int64_t ldg;
   typename E::T* Gt;
   int64_t ldgt;
-  const float* lse2;      // [R] row normaliser in base 2
+  const float* lse;       // [R] row normaliser, times lse_to2 in base 2
+  float lse_to2;          // 1 (base-2 input) or log2(e) (natural-log input)
   const uint8_t* mask;    // chunk rows, or nullptr
   const int* count;       // N
+  const float* grad_loss; // device scalar g, or nullptr for 1
   float tau, c2;
   int V, R;
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
-    const int N = *count;
-    const float s = N > 0 ? tau / (float)N : 0.f;
+    const float s = grad_scale(count, grad_loss, tau);
     // Rows past the vocabulary (z = 0 from zero-filled A rows) get finite
     // junk here: the head-gradient GEMM never reads G^T rows >= V, and the
     // hidden-gradient GEMM multiplies G's columns >= V by the zero columns of
@@ -144,7 +152,7 @@ struct EpiGrad {
       float sc = 0.f, l2 = 0.f;
       if (n < R) {
         if (!mask || mask[n]) sc = s;
-        l2 = lse2[n];
+        l2 = lse[n] * lse_to2;
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -544,20 +552,27 @@ __global__ __launch_bounds__(256) void chunk_loss_kernel(const double* rowkl, co
   if (threadIdx.x == 0) *loss_acc += s;
 }
 
-// Sparse teacher part of the logit gradient: G[t, id] -= (tau/N) m_t P[t, id]
-// for every distinct valid id of the row (duplicates summed first), in both
-// gradient layouts.  One block per chunk row.
+// Sparse teacher part of the logit gradient: G[t, id] -= g (tau/N) m_t
+// P[t, id] for every distinct valid id of the row (duplicates summed first),
+// in both gradient layouts.  One block per chunk row.  Invalid ids set
+// *status if status is not NULL (the backward-only call; otherwise the
+// forward's KL kernel reports them).
 template <class E>
 __global__ __launch_bounds__(128) void scatter_sparse_kernel(
-    const int32_t* idx, const float* logit, const uint8_t* mask, int K, int V, float tau,
-    const int* count, typename E::T* G, int64_t ldg, typename E::T* Gt, int64_t ldgt) {
+    const int32_t* idx, const float* logit, const uint8_t* mask, int K, int V, float tau, const int* count,
+    const float* grad_loss, typename E::T* G, int64_t ldg, typename E::T* Gt, int64_t ldgt, int32_t* status) {
   __shared__ float s_a[kMaxK];
   __shared__ int s_id[kMaxK];
   __shared__ float s_red[128];
   const int t = blockIdx.x;
-  const int N = *count;
-  if (N == 0 || (mask && !mask[t])) return;
-  const float s = tau / (float)N;
+  if (status) {
+    for (int k = threadIdx.x; k < K; k += 128) {
+      const int id = idx[(int64_t)t * K + k];
+      if (id < 0 || id >= V) *status = 7;   // KD_ERR_BAD_INDEX
+    }
+  }
+  if (*count == 0 || (mask && !mask[t])) return;
+  const float s = grad_scale(count, grad_loss, tau);
   const float inv_tau = 1.f / tau;
   for (int k = threadIdx.x; k < K; k += 128) s_id[k] = idx[(int64_t)t * K + k];
   const float lse_a = teacher_row<128>(logit + (int64_t)t * K, K, inv_tau, s_a, s_red);
@@ -579,17 +594,28 @@ __global__ __launch_bounds__(128) void scatter_sparse_kernel(
   }
 }
 
-// grad_hidden rows of the chunk: fixed-order sum of the split-K partials.
+// grad_hidden rows of the chunk: fixed-order sum of the split-K partials,
+// stored as fp32 or (OutT = uint16_t) bf16 with round to nearest even.
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+
+template <class OutT>
 __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* part, int64_t ldp, int64_t split_stride,
-                                                        int splits, int R, int d, float* out, int64_t ldo) {
+                                                        int splits, int R, int d, OutT* out, int64_t ldo) {
   const int64_t n = (int64_t)R * d;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int64_t t = i / d, j = i - t * d;
     const float* p = part + t * ldp + j;
     float s = 0.f;
     for (int sp = 0; sp < splits; ++sp) s += p[(int64_t)sp * split_stride];
-    out[t * ldo + j] = s;
+    store_out(out + t * ldo + j, s);
   }
+}
+
+// bf16 copy (round to nearest even) of an fp32 array.
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* src, uint16_t* dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = f32_to_bf16(src[i]);
 }
 
 __global__ void finalize_kernel(const double* loss_acc, const int* count, float tau, float* loss) {

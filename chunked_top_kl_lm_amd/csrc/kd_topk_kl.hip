@@ -59,7 +59,14 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// What a call computes: the fused forward + backward, the forward alone
+// (loss and the saved per-row logsumexp), or the backward alone (recomputed
+// from that logsumexp).
+enum Mode { kFused = 0, kForward = 1, kBackward = 2 };
+
 struct Plan {
+  int mode;
+  bool fwd, bwd;      // the call runs the forward steps / the backward steps
   int64_t T, d, V, K, chunk, nchunks;
   int eb;             // element bytes
   bool pad_d;         // d is not a multiple of 64: use zero-padded copies
@@ -67,20 +74,23 @@ struct Plan {
   int dh_bn, dw_bn;   // column tile (over d) of the hidden- and head-gradient GEMMs
   int64_t nvt;        // LSE strips per row
   int splits;         // split-K factor of the hidden-gradient GEMM
-  // workspace offsets
   int64_t nbt, nhb;   // teacher-id hit lists: row groups per chunk, lists per chunk
   int64_t nhb_p;      // nhb padded for the scan
   int64_t ng;         // first-level LSE merge groups per row
+  // workspace offsets (buffers a mode does not use take no space)
   size_t off_scalar, off_wt, off_wp, off_hp, off_ht, off_g, off_gt, off_part, off_lse2, off_rowkl, off_dh;
   size_t off_hcnt, off_hoff, off_hcur, off_hits, off_zsel, off_part2;
   size_t total;
 };
 
-int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t dt, Plan* p) {
+int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t dt, int mode, Plan* p) {
   if (dt != KD_BF16 && dt != KD_F32) return KD_ERR_DTYPE;
   if (T < 1 || d < 1 || V < 1 || K < 1 || K > V || K > KD_MAX_K) return KD_ERR_BAD_SHAPE;
   if (chunk < 1) return KD_ERR_BAD_CHUNK;
   Plan& P = *p;
+  P.mode = mode;
+  P.fwd = mode != kBackward;
+  P.bwd = mode != kForward;
   P.T = T; P.d = d; P.V = V; P.K = K;
   P.chunk = chunk > T ? T : chunk;
   P.nchunks = cdiv(T, P.chunk);
@@ -124,24 +134,29 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.splits = (int)cdiv(k_tiles, kps);
 
   const size_t e = (size_t)P.eb;
+  const bool F = P.fwd, B = P.bwd;
   size_t o = 0;
+  auto take = [&](size_t& off, bool used, size_t bytes) {
+    off = o;
+    if (used) o = align256(o + bytes);
+  };
   P.off_scalar = o; o += 256;
-  P.off_wt = o; o = align256(o + (size_t)P.d_p * P.V_p * e);
-  P.off_wp = o; if (P.pad_d) o = align256(o + (size_t)V * P.d_p * e);
-  P.off_hp = o; if (P.pad_d) o = align256(o + (size_t)P.R_p * P.d_p * e);
-  P.off_ht = o; o = align256(o + (size_t)P.d_p * P.R_p * e);
-  P.off_g = o; o = align256(o + (size_t)P.R_p * P.V_p * e);
-  P.off_gt = o; o = align256(o + (size_t)P.V_p * P.R_p * e);
-  P.off_part = o; o = align256(o + (size_t)P.nvt * P.R_p * sizeof(float2));
-  P.off_lse2 = o; o = align256(o + (size_t)P.R_p * sizeof(float));
-  P.off_rowkl = o; o = align256(o + (size_t)P.R_p * sizeof(double));
-  P.off_dh = o; o = align256(o + (size_t)P.splits * P.R_p * P.Nd_p * sizeof(float));
-  P.off_hcnt = o; o = align256(o + (size_t)P.nhb_p * sizeof(int));
-  P.off_hoff = o; o = align256(o + (size_t)(P.nhb_p + 1) * sizeof(int));
-  P.off_hcur = o; o = align256(o + (size_t)P.nhb_p * sizeof(int));
-  P.off_hits = o; o = align256(o + (size_t)P.R_p * K * sizeof(uint2));
-  P.off_zsel = o; o = align256(o + (size_t)P.R_p * K * sizeof(float));
-  P.off_part2 = o; o = align256(o + (size_t)P.ng * P.R_p * sizeof(float2));
+  take(P.off_wt, B, (size_t)P.d_p * P.V_p * e);
+  take(P.off_wp, P.pad_d, (size_t)V * P.d_p * e);
+  take(P.off_hp, P.pad_d, (size_t)P.R_p * P.d_p * e);
+  take(P.off_ht, B, (size_t)P.d_p * P.R_p * e);
+  take(P.off_g, B, (size_t)P.R_p * P.V_p * e);
+  take(P.off_gt, B, (size_t)P.V_p * P.R_p * e);
+  take(P.off_part, F, (size_t)P.nvt * P.R_p * sizeof(float2));
+  take(P.off_lse2, F, (size_t)P.R_p * sizeof(float));
+  take(P.off_rowkl, F, (size_t)P.R_p * sizeof(double));
+  take(P.off_dh, B, (size_t)P.splits * P.R_p * P.Nd_p * sizeof(float));
+  take(P.off_hcnt, F, (size_t)P.nhb_p * sizeof(int));
+  take(P.off_hoff, F, (size_t)(P.nhb_p + 1) * sizeof(int));
+  take(P.off_hcur, F, (size_t)P.nhb_p * sizeof(int));
+  take(P.off_hits, F, (size_t)P.R_p * K * sizeof(uint2));
+  take(P.off_zsel, F, (size_t)P.R_p * K * sizeof(float));
+  take(P.off_part2, F, (size_t)P.ng * P.R_p * sizeof(float2));
   P.total = o;
   return KD_OK;
 }
@@ -178,14 +193,35 @@ GemmShape make_shape(const void* A, int64_t lda, int M, const void* B, int64_t l
     if (hipGetLastError() != hipSuccess) return KD_ERR_HIP; \
   } while (0)
 
+// Pointers of one call (see the entry points for which a mode uses).
+struct Args {
+  const void* hidden;
+  const void* W;
+  const int32_t* idx;
+  const float* logit;
+  const uint8_t* mask;
+  float tau;
+  float* loss;             // fused, forward
+  float* row_lse;          // fused, forward: output (may be NULL in fused); backward: input
+  float* row_kl;           // fused, forward: output or NULL
+  const float* grad_loss;  // backward: device scalar dL/dloss, or NULL for 1
+  void* grad_hidden;       // fused, backward (NULL in backward: not computed)
+  int32_t gh_dtype;        // KD_F32 or KD_BF16
+  float* grad_W;           // fused, backward (NULL in backward: not computed)
+  int accumulate_W;        // backward: add into grad_W instead of overwriting it
+  uint16_t* grad_W_bf16;   // backward: optional bf16 copy of the final grad_W
+  int32_t* status;
+  hipStream_t st;
+  void* const* events;     // fused timing markers or NULL
+};
+
 template <class E>
-int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx, const float* logit,
-            const uint8_t* mask, float tau, float* loss, float* grad_hidden, float* grad_W, float* row_lse,
-            float* row_kl, char* ws, int32_t* status, hipStream_t st, void* const* events) {
+int32_t run(const Plan& P, const Args& A, char* ws) {
   typedef typename E::T T;
+  hipStream_t st = A.st;
   // timing markers (measurement entry point only)
   auto mark = [&](int64_t slot, int end) {
-    if (events) hipEventRecord((hipEvent_t)events[2 * slot + end], st);
+    if (A.events) hipEventRecord((hipEvent_t)A.events[2 * slot + end], st);
   };
   const int64_t pro_slot = (int64_t)KD_NUM_PHASES * P.nchunks;
   int* count = (int*)(ws + P.off_scalar);
@@ -208,24 +244,30 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
   float2* part2 = (float2*)(ws + P.off_part2);
 
   const int64_t T_ = P.T, d = P.d, V = P.V, K = P.K;
+  const float tau = A.tau;
   const float c2 = kLog2e / tau;
+  const bool want_dh = P.bwd && A.grad_hidden, want_dw = P.bwd && A.grad_W;
 
   mark(pro_slot, 0);
-  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, st, mask, T_, count, loss_acc, status);
+  hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, st, A.mask, T_, count, loss_acc, A.status);
   KD_LAUNCH_CHECK();
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(P.nhb_p, 256), 4096)), dim3(256), 0, st,
-                     hcnt, P.nhb_p, 0);
-  KD_LAUNCH_CHECK();
-  // W^T, zero-padded to [d_p][V_p]
-  hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.V_p / 64), (unsigned)(P.d_p / 64)), dim3(256), 0,
-                     st, (const T*)W, d, V, d, Wt, P.V_p);
-  KD_LAUNCH_CHECK();
-  const T* Wsrc = (const T*)W;
+  if (P.fwd) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(P.nhb_p, 256), 4096)), dim3(256), 0,
+                       st, hcnt, P.nhb_p, 0);
+    KD_LAUNCH_CHECK();
+  }
+  if (want_dh) {
+    // W^T, zero-padded to [d_p][V_p]
+    hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.V_p / 64), (unsigned)(P.d_p / 64)), dim3(256), 0,
+                       st, (const T*)A.W, d, V, d, Wt, P.V_p);
+    KD_LAUNCH_CHECK();
+  }
+  const T* Wsrc = (const T*)A.W;
   int64_t ldw = d;
   if (P.pad_d) {
     const int64_t n = V * P.d_p;
     hipLaunchKernelGGL(pad_kernel<E>, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
-                       (const T*)W, d, V, d, Wp, P.d_p, V);
+                       (const T*)A.W, d, V, d, Wp, P.d_p, V);
     KD_LAUNCH_CHECK();
     Wsrc = Wp;
     ldw = P.d_p;
@@ -238,8 +280,11 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     const int R = (int)std::min<int64_t>(P.chunk, T_ - c0);
     const int64_t Rt = round_up(R, kBN);     // rows covered by the GEMM tiles this chunk
     const int64_t slot = c * KD_NUM_PHASES;
+    const uint8_t* mask_c = A.mask ? A.mask + c0 : nullptr;
+    const int32_t* idx_c = A.idx + c0 * K;
+    const float* logit_c = A.logit + c0 * K;
     mark(slot + 0, 0);
-    const T* Hc = (const T*)hidden + c0 * d;
+    const T* Hc = (const T*)A.hidden + c0 * d;
     const T* Hsrc = Hc;
     int64_t ldh = d;
     if (P.pad_d) {
@@ -250,15 +295,14 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
       Hsrc = Hp;
       ldh = P.d_p;
     }
-    // H_c^T, zero-padded to [d_p][R_p]
-    hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.R_p / 64), (unsigned)(P.d_p / 64)), dim3(256), 0,
-                       st, Hc, d, (int64_t)R, d, Ht, P.R_p);
-    KD_LAUNCH_CHECK();
-    const uint8_t* mask_c = mask ? mask + c0 : nullptr;
-    const int32_t* idx_c = idx + c0 * K;
-    const float* logit_c = logit + c0 * K;
-    // teacher-id hit lists for the forward epilogue
-    {
+    if (want_dw) {
+      // H_c^T, zero-padded to [d_p][R_p]
+      hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.R_p / 64), (unsigned)(P.d_p / 64)), dim3(256),
+                         0, st, Hc, d, (int64_t)R, d, Ht, P.R_p);
+      KD_LAUNCH_CHECK();
+    }
+    if (P.fwd) {
+      // teacher-id hit lists for the forward epilogue
       const unsigned nblk = (unsigned)std::min<int64_t>(cdiv((int64_t)R * K, 256), 4096);
       hipLaunchKernelGGL(hit_count_kernel, dim3(nblk), dim3(256), 0, st, idx_c, R, (int)K, (int)V, (int)P.nbt, hcnt);
       KD_LAUNCH_CHECK();
@@ -270,42 +314,49 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
     }
     mark(slot + 0, 1);
 
-
-    // forward: z^T = W H_c^T -> LSE partials
-    mark(slot + 1, 0);
-    {
-      GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-      EpiLsePartial epi{part, (int)P.R_p, (int)V, c2, hoff, hits, zsel, (int)P.nbt};
-      if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+    if (P.fwd) {
+      // forward: z^T = W H_c^T -> LSE partials, z at the teacher ids
+      mark(slot + 1, 0);
+      {
+        GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
+        EpiLsePartial epi{part, (int)P.R_p, (int)V, c2, hoff, hits, zsel, (int)P.nbt};
+        if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      }
+      mark(slot + 1, 1);
+      mark(slot + 2, 0);
+      hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)cdiv(R, 32), (unsigned)P.ng), dim3(256), 0, st,
+                         (const float2*)part, (int)P.R_p, (int)P.nvt, R, part2);
+      KD_LAUNCH_CHECK();
+      hipLaunchKernelGGL(kl_rows_kernel, dim3(R), dim3(256), 0, st, (const float2*)part2, (int)P.R_p, (int)P.ng,
+                         lse2, A.row_lse ? A.row_lse + c0 : nullptr, (const float*)zsel, idx_c, logit_c, (int)K,
+                         (int)V, tau, rowkl, A.row_kl ? A.row_kl + c0 : nullptr, A.status);
+      KD_LAUNCH_CHECK();
+      hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(256), 0, st, (const double*)rowkl, mask_c, R, loss_acc);
+      KD_LAUNCH_CHECK();
+      mark(slot + 2, 1);
     }
-    mark(slot + 1, 1);
-    mark(slot + 2, 0);
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)cdiv(R, 32), (unsigned)P.ng), dim3(256), 0, st,
-                       (const float2*)part, (int)P.R_p, (int)P.nvt, R, part2);
-    KD_LAUNCH_CHECK();
-    hipLaunchKernelGGL(kl_rows_kernel, dim3(R), dim3(256), 0, st, (const float2*)part2, (int)P.R_p, (int)P.ng, lse2,
-                       row_lse ? row_lse + c0 : nullptr, (const float*)zsel, idx_c, logit_c, (int)K, (int)V, tau,
-                       rowkl, row_kl ? row_kl + c0 : nullptr, status);
-    KD_LAUNCH_CHECK();
-    hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(256), 0, st, (const double*)rowkl, mask_c, R, loss_acc);
-    KD_LAUNCH_CHECK();
-    mark(slot + 2, 1);
+    if (!P.bwd) continue;
+
     mark(slot + 3, 0);
-    // backward recompute: G = (tau/N) m q, both layouts
+    // backward recompute: G = (tau/N) m q, both layouts; the row normaliser
+    // comes from this call's forward (base 2) or from the saved row_lse
+    // (natural log)
     {
+      const float* lse_src = P.fwd ? (const float*)lse2 : (const float*)A.row_lse + c0;
+      const float lse_to2 = P.fwd ? 1.f : kLog2e;
       GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-      EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse2, mask_c, count, tau, c2, (int)V, R};
+      EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse_src, lse_to2, mask_c, count, A.grad_loss, tau, c2, (int)V, R};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 3, 1);
     mark(slot + 4, 0);
     hipLaunchKernelGGL(scatter_sparse_kernel<E>, dim3(R), dim3(128), 0, st, idx_c, logit_c, mask_c, (int)K, (int)V,
-                       tau, (const int*)count, G, P.V_p, Gt, P.R_p);
+                       tau, (const int*)count, A.grad_loss, G, P.V_p, Gt, P.R_p, P.fwd ? nullptr : A.status);
     KD_LAUNCH_CHECK();
     mark(slot + 4, 1);
-    mark(slot + 5, 0);
-    // dH_c = G W  (A = G [Rt x V_p], B = W^T [d x V_p]), split-K over V
-    {
+    if (want_dh) {
+      mark(slot + 5, 0);
+      // dH_c = G W  (A = G [Rt x V_p], B = W^T [d x V_p]), split-K over V
       EpiStoreSplit epi{dhp, P.Nd_p, P.R_p * P.Nd_p};
       GemmShape g;
       if (P.dh_bn == TileDhWide::BN) {
@@ -318,15 +369,20 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
       mark(slot + 5, 1);
       mark(slot + 6, 0);
       const int64_t n = (int64_t)R * d;
-      hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
-                         (const float*)dhp, P.Nd_p, P.R_p * P.Nd_p, g.splits, R, (int)d, grad_hidden + c0 * d, d);
+      const dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 65536));
+      if (A.gh_dtype == KD_BF16)
+        hipLaunchKernelGGL(dh_reduce_kernel<uint16_t>, grid, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
+                           P.R_p * P.Nd_p, g.splits, R, (int)d, (uint16_t*)A.grad_hidden + c0 * d, d);
+      else
+        hipLaunchKernelGGL(dh_reduce_kernel<float>, grid, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
+                           P.R_p * P.Nd_p, g.splits, R, (int)d, (float*)A.grad_hidden + c0 * d, d);
       KD_LAUNCH_CHECK();
       mark(slot + 6, 1);
     }
-    mark(slot + 7, 0);
-    // dW (+)= G^T H_c  (A = G^T [V_p x R_p], B = H_c^T [d x R_p])
-    {
-      EpiAccum epi{grad_W, d, (int)V, (int)d, c == 0 ? 1 : 0};
+    if (want_dw) {
+      mark(slot + 7, 0);
+      // dW (+)= G^T H_c  (A = G^T [V_p x R_p], B = H_c^T [d x R_p])
+      EpiAccum epi{A.grad_W, d, (int)V, (int)d, (c == 0 && !A.accumulate_W) ? 1 : 0};
       if (P.dw_bn == TileHead::BN) {
         GemmShape g = make_shape<TileHead>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
         if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
@@ -334,14 +390,41 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
         GemmShape g = make_shape<TileHeadNarrow>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
         if (launch_gemm<TileHeadNarrow, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
       }
+      mark(slot + 7, 1);
     }
-    mark(slot + 7, 1);
   }
   mark(pro_slot + 1, 0);
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, st, (const double*)loss_acc, (const int*)count, tau, loss);
-  KD_LAUNCH_CHECK();
+  if (P.fwd) {
+    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, st, (const double*)loss_acc, (const int*)count, tau,
+                       A.loss);
+    KD_LAUNCH_CHECK();
+  }
+  if (want_dw && A.grad_W_bf16) {
+    const int64_t n = V * d;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
+                       (const float*)A.grad_W, A.grad_W_bf16, n);
+    KD_LAUNCH_CHECK();
+  }
   mark(pro_slot + 1, 1);
   return KD_OK;
+}
+
+int32_t dispatch(int mode, int32_t in_dtype, int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                 void* workspace, size_t workspace_bytes, const Args& A) {
+  if (!(A.tau > 0.f) || !isfinite(A.tau)) return KD_ERR_BAD_TAU;
+  Plan p;
+  const int32_t st = make_plan(T, d, V, K, chunk, in_dtype, mode, &p);
+  if (st != KD_OK) return st;
+  if ((((uintptr_t)A.hidden) | ((uintptr_t)A.W)) & 15) return KD_ERR_BAD_SHAPE;
+  if (!workspace || workspace_bytes < p.total || (((uintptr_t)workspace) & 255)) return KD_ERR_WORKSPACE;
+  if (in_dtype == KD_BF16) return run<Bf16>(p, A, (char*)workspace);
+  return run<F32>(p, A, (char*)workspace);
+}
+
+size_t workspace_for(int mode, int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
+  Plan p;
+  if (make_plan(T, d, V, K, chunk, in_dtype, mode, &p) != KD_OK) return 0;
+  return p.total;
 }
 
 }  // namespace
@@ -350,9 +433,15 @@ int32_t run(const Plan& P, const void* hidden, const void* W, const int32_t* idx
 extern "C" {
 
 size_t kd_topk_kl_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
-  kd::Plan p;
-  if (kd::make_plan(T, d, V, K, chunk, in_dtype, &p) != KD_OK) return 0;
-  return p.total;
+  return kd::workspace_for(kd::kFused, T, d, V, K, chunk, in_dtype);
+}
+
+size_t kd_topk_kl_fwd_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
+  return kd::workspace_for(kd::kForward, T, d, V, K, chunk, in_dtype);
+}
+
+size_t kd_topk_kl_bwd_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
+  return kd::workspace_for(kd::kBackward, T, d, V, K, chunk, in_dtype);
 }
 
 static int32_t fwd_bwd_impl(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
@@ -361,18 +450,9 @@ static int32_t fwd_bwd_impl(const void* hidden, const void* W, int32_t in_dtype,
                             float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,
                             int32_t* status_dev, void* stream, void* const* events) {
   if (!hidden || !W || !teacher_idx || !teacher_logit || !loss || !grad_hidden || !grad_W) return KD_ERR_NULL_ARG;
-  if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_BAD_TAU;
-  kd::Plan p;
-  const int32_t st = kd::make_plan(T, d, V, K, chunk, in_dtype, &p);
-  if (st != KD_OK) return st;
-  if ((((uintptr_t)hidden) | ((uintptr_t)W)) & 15) return KD_ERR_BAD_SHAPE;
-  if (!workspace || workspace_bytes < p.total || (((uintptr_t)workspace) & 255)) return KD_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  if (in_dtype == KD_BF16)
-    return kd::run<kd::Bf16>(p, hidden, W, teacher_idx, teacher_logit, mask, tau, loss, grad_hidden, grad_W, row_lse,
-                             row_kl, (char*)workspace, status_dev, s, events);
-  return kd::run<kd::F32>(p, hidden, W, teacher_idx, teacher_logit, mask, tau, loss, grad_hidden, grad_W, row_lse,
-                          row_kl, (char*)workspace, status_dev, s, events);
+  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, loss, row_lse, row_kl, nullptr, grad_hidden, KD_F32,
+             grad_W, 0, nullptr, status_dev, (hipStream_t)stream, events};
+  return kd::dispatch(kd::kFused, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
 }
 
 int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
@@ -394,6 +474,31 @@ int32_t kd_topk_kl_fwd_bwd_timed(const void* hidden, const void* W, int32_t in_d
                       grad_hidden, grad_W, row_lse, row_kl, workspace, workspace_bytes, status_dev, stream, events);
 }
 
+int32_t kd_topk_kl_fwd(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                       const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                       float tau, int64_t chunk, float* loss, float* row_lse, float* row_kl, void* workspace,
+                       size_t workspace_bytes, int32_t* status_dev, void* stream) {
+  if (!hidden || !W || !teacher_idx || !teacher_logit || !loss || !row_lse) return KD_ERR_NULL_ARG;
+  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, loss, row_lse, row_kl, nullptr, nullptr, KD_F32,
+             nullptr, 0, nullptr, status_dev, (hipStream_t)stream, nullptr};
+  return kd::dispatch(kd::kForward, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
+}
+
+int32_t kd_topk_kl_bwd(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                       const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                       float tau, int64_t chunk, const float* row_lse, const float* grad_loss, void* grad_hidden,
+                       int32_t grad_hidden_dtype, float* grad_W, int32_t accumulate_grad_W, uint16_t* grad_W_bf16,
+                       void* workspace, size_t workspace_bytes, int32_t* status_dev, void* stream) {
+  if (!hidden || !W || !teacher_idx || !teacher_logit || !row_lse) return KD_ERR_NULL_ARG;
+  if (!grad_hidden && !grad_W) return KD_ERR_NULL_ARG;
+  if (grad_W_bf16 && !grad_W) return KD_ERR_NULL_ARG;
+  if (grad_hidden_dtype != KD_F32 && grad_hidden_dtype != KD_BF16) return KD_ERR_DTYPE;
+  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, nullptr, const_cast<float*>(row_lse), nullptr,
+             grad_loss, grad_hidden, grad_hidden_dtype, grad_W, accumulate_grad_W ? 1 : 0, grad_W_bf16, status_dev,
+             (hipStream_t)stream, nullptr};
+  return kd::dispatch(kd::kBackward, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
+}
+
 const char* kd_status_str(int32_t s) {
   switch (s) {
     case KD_OK: return "ok";
@@ -401,7 +506,7 @@ const char* kd_status_str(int32_t s) {
     case KD_ERR_BAD_SHAPE: return "bad shape (T, d, V, K < 1, K > V, K > KD_MAX_K, too large, or misaligned input)";
     case KD_ERR_BAD_TAU: return "tau must be finite and > 0";
     case KD_ERR_BAD_CHUNK: return "chunk must be >= 1";
-    case KD_ERR_DTYPE: return "in_dtype must be KD_BF16 or KD_F32";
+    case KD_ERR_DTYPE: return "in_dtype (or the gradient output dtype) must be KD_BF16 or KD_F32";
     case KD_ERR_WORKSPACE: return "workspace is NULL, too small or not 256-byte aligned";
     case KD_ERR_BAD_INDEX: return "a teacher id is outside [0, V)";
     case KD_ERR_HIP: return "a HIP launch failed";

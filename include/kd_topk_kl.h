@@ -149,6 +149,67 @@ int32_t kd_topk_kl_fwd_bwd_timed(const void* hidden, const void* W, int32_t in_d
                                  int32_t* status_dev, void* stream,
                                  void* const* events);
 
+/*
+ * Split entry points, for a training step whose forward and backward are
+ * separate calls (the loss sits inside a model and the backward runs when
+ * the framework back-propagates).  The method is the same: the forward
+ * projects one chunk at a time, folds it into the loss and discards it, and
+ * the backward rebuilds each chunk's logits when it needs them (the second
+ * half of the fix described on the same Glonce page, paragraph on
+ * Multiverse's two-part fix).  The only state carried from the forward to
+ * the backward is the per-row logsumexp, O(T) floats.
+ *
+ * Workspace sizes for the two calls (0 if the arguments are invalid); each
+ * is at most that of the fused call, and neither depends on T beyond the
+ * chunk.
+ */
+size_t kd_topk_kl_fwd_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K,
+                                      int64_t chunk, int32_t in_dtype);
+size_t kd_topk_kl_bwd_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K,
+                                      int64_t chunk, int32_t in_dtype);
+
+/*
+ * Forward only: `loss` (device fp32 scalar) and `row_lse` (device [T] fp32,
+ * required: logsumexp_v S[t,:], to be passed to kd_topk_kl_bwd), `row_kl`
+ * optional as in kd_topk_kl_fwd_bwd.  Inputs, workspace, status and stream
+ * as for kd_topk_kl_fwd_bwd (workspace of kd_topk_kl_fwd_workspace_bytes).
+ * The loss and row statistics are bitwise those of the fused call.
+ */
+int32_t kd_topk_kl_fwd(const void* hidden, const void* W, int32_t in_dtype,
+                       const int32_t* teacher_idx, const float* teacher_logit,
+                       const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                       float tau, int64_t chunk,
+                       float* loss, float* row_lse, float* row_kl,
+                       void* workspace, size_t workspace_bytes,
+                       int32_t* status_dev, void* stream);
+
+/*
+ * Backward only: the gradients of g * loss, with g = *grad_loss (device fp32
+ * scalar; NULL means 1), recomputing every chunk's logits.
+ *  row_lse            device [T] fp32 from kd_topk_kl_fwd on the same inputs.
+ *  grad_hidden        device [T, d] of grad_hidden_dtype (KD_F32, or KD_BF16
+ *                     rounded to nearest even), overwritten; NULL: not
+ *                     computed (its GEMM is skipped).
+ *  grad_W             device [V, d] fp32; overwritten, or, with
+ *                     accumulate_grad_W != 0, added to (fp32 accumulation,
+ *                     e.g. across micro-batches); NULL: not computed.
+ *  grad_W_bf16        device [V, d] bf16 or NULL: a copy of the final grad_W
+ *                     rounded to nearest even (requires grad_W).
+ * At least one of grad_hidden and grad_W must be given (else
+ * KD_ERR_NULL_ARG); KD_ERR_DTYPE for another grad_hidden_dtype.  Inputs,
+ * workspace (kd_topk_kl_bwd_workspace_bytes), status and stream as for
+ * kd_topk_kl_fwd_bwd; invalid ids are reported here too.
+ */
+int32_t kd_topk_kl_bwd(const void* hidden, const void* W, int32_t in_dtype,
+                       const int32_t* teacher_idx, const float* teacher_logit,
+                       const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                       float tau, int64_t chunk,
+                       const float* row_lse, const float* grad_loss,
+                       void* grad_hidden, int32_t grad_hidden_dtype,
+                       float* grad_W, int32_t accumulate_grad_W, uint16_t* grad_W_bf16,
+                       void* workspace, size_t workspace_bytes,
+                       int32_t* status_dev, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kd_status_str(int32_t status);
 

@@ -20,7 +20,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {"kd_topk_kl_workspace_bytes", "kd_topk_kl_fwd_bwd",
-                                          "kd_topk_kl_fwd_bwd_timed", "kd_status_str"}
+                                          "kd_topk_kl_fwd_bwd_timed", "kd_status_str",
+                                          "kd_topk_kl_fwd_workspace_bytes", "kd_topk_kl_bwd_workspace_bytes",
+                                          "kd_topk_kl_fwd", "kd_topk_kl_bwd"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -92,3 +94,53 @@ def test_timed_entry_requires_events():
                                     1000, 10, 1.0, 32, v(0x50000), v(0x60000), v(0x70000), None, None,
                                     v(0x100000), 1 << 40, None, None, None)
     assert rc == 1
+
+
+def test_split_workspaces():
+    shape = (32768, 2880, 201088, 100, 2048, 0)
+    fused, f, b = kd.workspace_bytes(*shape), kd.fwd_workspace_bytes(*shape), kd.bwd_workspace_bytes(*shape)
+    # the forward holds no chunk x V gradient buffer; the backward no forward statistics
+    assert 0 < f < 64 * 2**20 < b < fused
+    assert kd.fwd_workspace_bytes(0, 8, 8, 1, 1, 0) == 0 and kd.bwd_workspace_bytes(8, 8, 8, 9, 1, 0) == 0
+    big = (262144, 2880, 201088, 100, 2048, 0)
+    assert kd.fwd_workspace_bytes(*big) == f and kd.bwd_workspace_bytes(*big) == b
+
+
+def _call_fwd(**kw):
+    L = kd.lib()
+    a = dict(hidden=0x10000, W=0x20000, dt=0, idx=0x30000, logit=0x40000, mask=None, T=64, d=64, V=1000,
+             K=10, tau=1.0, chunk=32, loss=0x50000, rl=0x60000, rk=None, ws=0x100000, wsb=1 << 40)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kd_topk_kl_fwd(v(a["hidden"]), v(a["W"]), a["dt"], v(a["idx"]), v(a["logit"]), v(a["mask"]),
+                            a["T"], a["d"], a["V"], a["K"], a["tau"], a["chunk"], v(a["loss"]), v(a["rl"]),
+                            v(a["rk"]), v(a["ws"]), a["wsb"], None, None)
+
+
+def _call_bwd(**kw):
+    L = kd.lib()
+    a = dict(hidden=0x10000, W=0x20000, dt=0, idx=0x30000, logit=0x40000, mask=None, T=64, d=64, V=1000,
+             K=10, tau=1.0, chunk=32, rl=0x60000, gl=None, gH=0x70000, ghdt=1, gW=0x80000, acc=0, gWb=None,
+             ws=0x100000, wsb=1 << 40)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kd_topk_kl_bwd(v(a["hidden"]), v(a["W"]), a["dt"], v(a["idx"]), v(a["logit"]), v(a["mask"]),
+                            a["T"], a["d"], a["V"], a["K"], a["tau"], a["chunk"], v(a["rl"]), v(a["gl"]),
+                            v(a["gH"]), a["ghdt"], v(a["gW"]), a["acc"], v(a["gWb"]), v(a["ws"]), a["wsb"],
+                            None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=None), 1), (dict(loss=None), 1), (dict(rl=None), 1), (dict(tau=0.0), 3),
+    (dict(K=0), 2), (dict(chunk=0), 4), (dict(dt=2), 5), (dict(ws=None), 6), (dict(wsb=10), 6),
+])
+def test_fwd_host_argument_errors(kw, code):
+    assert _call_fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=None), 1), (dict(rl=None), 1), (dict(gH=None, gW=None), 1), (dict(gW=None, gWb=0x90000), 1),
+    (dict(ghdt=2), 5), (dict(tau=float("nan")), 3), (dict(V=0), 2), (dict(dt=9), 5), (dict(ws=0x100008), 6),
+])
+def test_bwd_host_argument_errors(kw, code):
+    assert _call_bwd(**kw) == code
