@@ -125,7 +125,9 @@ struct EpiCtx {
   int split;
   int tm, tn;
   int wm, wn;
-  char* smem;   // the LDS ring (free once the main loop has ended)
+  int wid, nwaves;
+  char* smem;       // the LDS ring (free once the main loop has ended)
+  int smem_bytes;   // its size
 };
 
 // ---------------------------------------------------------------------------
@@ -383,7 +385,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
   ctx.tn = pos.tn;
   ctx.wm = wm;
   ctx.wn = wn;
+  ctx.wid = wid;
+  ctx.nwaves = C::NW;
   ctx.smem = smem;
+  ctx.smem_bytes = C::kLds;
   epi.template apply<C::FM, C::FN>(acc, ctx);
 }
 
