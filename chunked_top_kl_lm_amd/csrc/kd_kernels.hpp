@@ -116,8 +116,9 @@ struct EpiLsePartial {
 // G[t,v] = g (tau/N) m_t q[t,v] (g = dL/dloss from the caller, 1 in the
 // fused call), written in two layouts (G [R_p][V_p] and G^T [V_p][R_p]) for
 // the two gradient GEMMs; entries at v >= V are unused.  The sparse teacher
-// part -g (tau/N) m_t P[t,v] is subtracted afterwards by
-// scatter_sparse_kernel.
+// part -g (tau/N) m_t P[t,v] is subtracted in the epilogue from the fp32
+// values (fused call, through the forward's hit lists) or afterwards by
+// scatter_sparse_kernel (backward-only call).
 __device__ __forceinline__ float grad_scale(const int* count, const float* grad_loss, float tau) {
   const int N = *count;
   return N > 0 ? (grad_loss ? *grad_loss : 1.f) * (tau / (float)N) : 0.f;
@@ -136,16 +137,36 @@ struct EpiGrad {
   const float* grad_loss; // device scalar g, or nullptr for 1
   float tau, c2;
   int V, R;
+  // The sparse teacher part in the epilogue (fused call): the forward's
+  // teacher-id hit lists and the teacher probabilities psel[t*K + k]; with
+  // hit_off == nullptr it is left to scatter_sparse_kernel.
+  const int* hit_off;
+  const uint2* hits;
+  const float* psel;
+  int nbt;
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    // G values in fp32, in place: acc <- sc * q (sc = g tau m_t / N)
+    const float s = grad_scale(count, grad_loss, tau);
+    float sc[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      float l2;
+      column(c.n0 + 32 * j + acc_col(c.lane), s, sc[j], l2);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = sc[j] * fast_exp2(fminf(acc[i][j][r] * c2 - l2, 0.f));
+    }
+    if (hit_off) sparse_part<FM, FN>(acc, sc, c);
     if constexpr (E::kBytes == 2 && FM == 4 && FN == 2) {
       if (c.smem_bytes / c.nwaves >= kStageBytes) {
-        apply_staged(acc, c);
+        store_staged(acc, c);
         return;
       }
     }
-    apply_direct<FM, FN>(acc, c);
+    store_direct<FM, FN>(acc, c);
   }
 
   // Row scale and base-2 normaliser of the lane's column n.
@@ -158,20 +179,42 @@ struct EpiGrad {
     }
   }
 
-  // Rows past the vocabulary (z = 0 from zero-filled A rows) get finite junk
-  // in both paths: the head-gradient GEMM never reads G^T rows >= V, and the
-  // hidden-gradient GEMM multiplies G's columns >= V by the zero columns of
-  // the padded W^T.  Capping the exponent at 0 keeps them finite (for real
-  // rows x*c2 <= lse2 holds up to the rounding of the normaliser, since both
-  // passes produce the same z and the merged sum is >= 1).
+  // -sc_t p_k at (v = idx[t,k], t) for every (t, k) filed under this wave
+  // tile (duplicate ids each subtract their own p, so P sums them); the
+  // lane that holds the element applies it, so G is rounded once.
   template <int FM, int FN>
-  __device__ __forceinline__ void apply_direct(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
-    const float s = grad_scale(count, grad_loss, tau);
+  __device__ __forceinline__ void sparse_part(f32x16 (&acc)[FM][FN], const float (&sc)[FN], const EpiCtx& c) const {
+    static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
+    const int b = (c.m0 / kHitV) * nbt + c.n0 / kHitT;
+    const int e1 = hit_off[b + 1];
+    for (int e = hit_off[b]; e < e1; ++e) {
+      const uint2 h = hits[e];
+      const int vl = (int)(h.y >> 6), tl = (int)(h.y & 63);
+      const int rr = vl & 31;
+      const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
+      const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
+      const float p = psel[h.x];
+      if (c.lane == owner) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (i == (vl >> 5) && j == (tl >> 5)) acc[i][j][r] -= sc[j] * p;
+      }
+    }
+  }
+
+  // Rows past the vocabulary (z = 0 from zero-filled A rows) get finite junk
+  // in both store paths: the head-gradient GEMM never reads G^T rows >= V,
+  // and the hidden-gradient GEMM multiplies G's columns >= V by the zero
+  // columns of the padded W^T.  Capping the exponent at 0 keeps them finite
+  // (for real rows x*c2 <= lse2 holds up to the rounding of the normaliser,
+  // since both passes produce the same z and the merged sum is >= 1).
+  template <int FM, int FN>
+  __device__ __forceinline__ void store_direct(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = c.n0 + 32 * j + acc_col(c.lane);
-      float sc, l2;
-      column(n, s, sc, l2);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -179,7 +222,7 @@ struct EpiGrad {
           const int v0 = c.m0 + 32 * i + 8 * g4 + 4 * (c.lane >> 5);
           float gv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) gv[e] = sc * fast_exp2(fminf(acc[i][j][4 * g4 + e] * c2 - l2, 0.f));
+          for (int e = 0; e < 4; ++e) gv[e] = acc[i][j][4 * g4 + e];
           store4(G + (int64_t)n * ldg + v0, gv);
 #pragma unroll
           for (int e = 0; e < 4; ++e) Gt[(int64_t)(v0 + e) * ldgt + n] = store_cvt<E>(gv[e]);
@@ -190,8 +233,8 @@ struct EpiGrad {
   // bf16 with 128 x 64 wave tiles: the wave's tile goes through its own
   // 16 KB of the (now free) LDS ring twice, once per layout, so that both
   // layouts leave as 16-byte stores of whole 128/256-byte row segments
-  // instead of 8-byte and 2-byte scattered stores.  Measured on the 32K
-  // workload's recompute GEMM: 0.07 ms less per launch than the direct path.
+  // instead of 8-byte and 2-byte scattered stores (0.05-0.07 ms less per
+  // launch on the 32K workload's recompute GEMM).
   //   G staging  [64 t][128 v], 256-byte rows, 16-byte slot u of row t at
   //              u ^ (t & 15) (the 8-byte writes of a half-wave, 32 rows
   //              apart by 256 bytes, spread over the banks);
@@ -199,15 +242,12 @@ struct EpiGrad {
   //              rows with bit 2 set (the two half-waves write rows 4 apart).
   static constexpr int kStageBytes = 16384;
 
-  __device__ __forceinline__ void apply_staged(f32x16 (&acc)[4][2], const EpiCtx& c) const {
-    const float s = grad_scale(count, grad_loss, tau);
+  __device__ __forceinline__ void store_staged(f32x16 (&acc)[4][2], const EpiCtx& c) const {
     char* lds = c.smem + c.wid * (c.smem_bytes / c.nwaves);
     uint2 pk[4][2][4];   // bf16 values, 4 consecutive v per entry
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int tl = 32 * j + acc_col(c.lane);
-      float sc, l2;
-      column(c.n0 + tl, s, sc, l2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -215,8 +255,7 @@ struct EpiGrad {
           const int vl0 = 32 * i + 8 * g4 + 4 * (c.lane >> 5);
           uint16_t b[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            b[e] = f32_to_bf16(sc * fast_exp2(fminf(acc[i][j][4 * g4 + e] * c2 - l2, 0.f)));
+          for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16(acc[i][j][4 * g4 + e]);
           pk[i][j][g4] = make_uint2((uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16));
           *(uint2*)(lds + tl * 256 + (((vl0 >> 3) ^ (tl & 15)) << 4) + ((vl0 & 7) << 1)) = pk[i][j][g4];
         }
@@ -528,6 +567,45 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const typename E::T*
   }
 }
 
+// bf16 transpose with 16-byte loads and stores: dst[c][r] = src[r][c] for
+// r < rows, c < cols, zero elsewhere in the block's 64 x 64 destination
+// tile.  Requires ld_src and ld_dst multiples of 8 and 16-byte aligned
+// bases.
+__global__ __launch_bounds__(256) void transpose_bf16_vec_kernel(const uint16_t* src, int64_t ld_src, int64_t rows,
+                                                                 int64_t cols, uint16_t* dst, int64_t ld_dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // 144-byte rows
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = (t >> 3) + 32 * h, vc = t & 7;
+    const int64_t r = r0 + row, c = c0 + 8 * vc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows) {
+      if (c + 8 <= cols) {
+        v = *(const u32x4*)(src + r * ld_src + c);
+      } else if (c < cols) {
+        uint16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = c + e < cols ? src[r * ld_src + c + e] : (uint16_t)0;
+        v = u32x4{e8[0] | ((uint32_t)e8[1] << 16), e8[2] | ((uint32_t)e8[3] << 16), e8[4] | ((uint32_t)e8[5] << 16),
+                  e8[6] | ((uint32_t)e8[7] << 16)};
+      }
+    }
+    *(u32x4*)&tile[row][8 * vc] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int drow = (t >> 3) + 32 * h, vr = t & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[8 * vr + 2 * e][drow] | ((uint32_t)tile[8 * vr + 2 * e + 1][drow] << 16);
+    *(u32x4*)(dst + (c0 + drow) * ld_dst + r0 + 8 * vr) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 // dst[r][c] = src[r][c] for r < rows, c < cols; zero elsewhere in the
 // [dst_rows x ld_dst] destination.
 template <class E>
@@ -589,7 +667,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float2* part, int 
 __global__ __launch_bounds__(256) void kl_rows_kernel(const float2* part2, int ldp, int ng, float* lse2_out,
                                                       float* row_lse, const float* zsel, const int32_t* idx,
                                                       const float* logit, int K, int V, float tau, double* rowkl,
-                                                      float* row_kl, int32_t* status) {
+                                                      float* row_kl, float* psel, int32_t* status) {
   __shared__ float s_a[kMaxK];
   __shared__ float s_red[256];
   __shared__ double s_d[256];
@@ -621,6 +699,7 @@ __global__ __launch_bounds__(256) void kl_rows_kernel(const float2* part2, int l
     const float z = zsel[(int64_t)t * K + k];
     const float logp = s_a[k] - lse_a;
     const float p = expf(logp);
+    if (psel) psel[(int64_t)t * K + k] = p;   // the recompute epilogue's sparse part
     if (p > 0.f) kl += (double)p * ((double)logp - ((double)z * inv_tau - (double)lse));
   }
   kl = block_reduce<256>(kl, s_d, OpAddD());
@@ -698,6 +777,32 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* part, int64
     float s = 0.f;
     for (int sp = 0; sp < splits; ++sp) s += p[(int64_t)sp * split_stride];
     store_out(out + t * ldo + j, s);
+  }
+}
+
+// The same with 4 columns per thread (d, ldp and ldo multiples of 4, the
+// partial buffer and the output 16-byte / 8-byte aligned): one 16-byte load
+// per split, same fixed summation order.
+__device__ __forceinline__ void store_out4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ void store_out4(uint16_t* p, float4 v) {
+  *(uint2*)p = make_uint2((uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                          (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
+}
+
+template <class OutT>
+__global__ __launch_bounds__(256) void dh_reduce4_kernel(const float* part, int64_t ldp, int64_t split_stride,
+                                                         int splits, int R, int d, OutT* out, int64_t ldo) {
+  const int d4 = d >> 2;
+  const int64_t n = (int64_t)R * d4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / d4, j = 4 * (i - t * d4);
+    const float* p = part + t * ldp + j;
+    float4 s = *(const float4*)p;
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 v = *(const float4*)(p + (int64_t)sp * split_stride);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    store_out4(out + t * ldo + j, s);
   }
 }
 

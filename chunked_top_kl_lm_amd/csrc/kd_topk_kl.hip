@@ -15,8 +15,9 @@
 //                     z at the teacher ids picked from the accumulators
 //     KL rows         online merge -> LSE_t; teacher p; KL_t
 //     chunk loss      fixed-order fp64 sum of m_t KL_t
-//     GEMM + grad     recompute z^T, G = (tau/N) m q in two layouts
-//     scatter         G[t, id] -= (tau/N) m_t P[t, id]
+//     GEMM + grad     recompute z^T, G = (tau/N) m (q - P) in two layouts,
+//                     the sparse teacher part P at the hit lists' entries
+//   (the backward-only entry point subtracts P with a scatter kernel instead)
 //     GEMM dH         split-K over the vocabulary, fixed-order reduction
 //     GEMM dW         grad_W (+)= G^T H_c in fp32
 //   finalize        loss = tau^2 * acc / N
@@ -79,7 +80,7 @@ struct Plan {
   int64_t ng;         // first-level LSE merge groups per row
   // workspace offsets (buffers a mode does not use take no space)
   size_t off_scalar, off_wt, off_wp, off_hp, off_ht, off_g, off_gt, off_part, off_lse2, off_rowkl, off_dh;
-  size_t off_hcnt, off_hoff, off_hcur, off_hits, off_zsel, off_part2;
+  size_t off_hcnt, off_hoff, off_hcur, off_hits, off_zsel, off_part2, off_psel;
   size_t total;
 };
 
@@ -157,6 +158,7 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   take(P.off_hits, F, (size_t)P.R_p * K * sizeof(uint2));
   take(P.off_zsel, F, (size_t)P.R_p * K * sizeof(float));
   take(P.off_part2, F, (size_t)P.ng * P.R_p * sizeof(float2));
+  take(P.off_psel, F && B, (size_t)P.R_p * K * sizeof(float));   // teacher p for the fused sparse part
   P.total = o;
   return KD_OK;
 }
@@ -186,6 +188,20 @@ GemmShape make_shape(const void* A, int64_t lda, int M, const void* B, int64_t l
   g.tiles_m = (int)cdiv(M, TC::BM);
   g.tiles_n = (int)cdiv(N, TC::BN);
   return g;
+}
+
+// dst [gy*64 x ld_dst] = transpose of src [rows x cols] (ld_src), zero
+// padded; 16-byte accesses when the layout allows it.
+template <class E>
+void launch_transpose(const typename E::T* src, int64_t ld_src, int64_t rows, int64_t cols, typename E::T* dst,
+                      int64_t ld_dst, unsigned gx, unsigned gy, hipStream_t st) {
+  const bool vec = E::kBytes == 2 && ld_src % 8 == 0 && ld_dst % 8 == 0 &&
+                   ((((uintptr_t)src) | ((uintptr_t)dst)) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(transpose_bf16_vec_kernel, dim3(gx, gy), dim3(256), 0, st, (const uint16_t*)src, ld_src, rows,
+                       cols, (uint16_t*)dst, ld_dst);
+  else
+    hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3(gx, gy), dim3(256), 0, st, src, ld_src, rows, cols, dst, ld_dst);
 }
 
 #define KD_LAUNCH_CHECK()                         \
@@ -242,6 +258,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
   uint2* hits = (uint2*)(ws + P.off_hits);
   float* zsel = (float*)(ws + P.off_zsel);
   float2* part2 = (float2*)(ws + P.off_part2);
+  float* psel = (P.fwd && P.bwd) ? (float*)(ws + P.off_psel) : nullptr;
 
   const int64_t T_ = P.T, d = P.d, V = P.V, K = P.K;
   const float tau = A.tau;
@@ -258,8 +275,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
   }
   if (want_dh) {
     // W^T, zero-padded to [d_p][V_p]
-    hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.V_p / 64), (unsigned)(P.d_p / 64)), dim3(256), 0,
-                       st, (const T*)A.W, d, V, d, Wt, P.V_p);
+    launch_transpose<E>((const T*)A.W, d, V, d, Wt, P.V_p, (unsigned)(P.V_p / 64), (unsigned)(P.d_p / 64), st);
     KD_LAUNCH_CHECK();
   }
   const T* Wsrc = (const T*)A.W;
@@ -297,8 +313,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
     }
     if (want_dw) {
       // H_c^T, zero-padded to [d_p][R_p]
-      hipLaunchKernelGGL(transpose_pad_kernel<E>, dim3((unsigned)(P.R_p / 64), (unsigned)(P.d_p / 64)), dim3(256),
-                         0, st, Hc, d, (int64_t)R, d, Ht, P.R_p);
+      launch_transpose<E>(Hc, d, (int64_t)R, d, Ht, P.R_p, (unsigned)(P.R_p / 64), (unsigned)(P.d_p / 64), st);
       KD_LAUNCH_CHECK();
     }
     if (P.fwd) {
@@ -329,7 +344,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       KD_LAUNCH_CHECK();
       hipLaunchKernelGGL(kl_rows_kernel, dim3(R), dim3(256), 0, st, (const float2*)part2, (int)P.R_p, (int)P.ng,
                          lse2, A.row_lse ? A.row_lse + c0 : nullptr, (const float*)zsel, idx_c, logit_c, (int)K,
-                         (int)V, tau, rowkl, A.row_kl ? A.row_kl + c0 : nullptr, A.status);
+                         (int)V, tau, rowkl, A.row_kl ? A.row_kl + c0 : nullptr, psel, A.status);
       KD_LAUNCH_CHECK();
       hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(256), 0, st, (const double*)rowkl, mask_c, R, loss_acc);
       KD_LAUNCH_CHECK();
@@ -345,14 +360,18 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       const float* lse_src = P.fwd ? (const float*)lse2 : (const float*)A.row_lse + c0;
       const float lse_to2 = P.fwd ? 1.f : kLog2e;
       GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-      EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse_src, lse_to2, mask_c, count, A.grad_loss, tau, c2, (int)V, R};
+      // fused call: the sparse teacher part goes in the epilogue
+      EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse_src, lse_to2, mask_c, count, A.grad_loss, tau, c2, (int)V, R,
+                     psel ? hoff : nullptr, hits, psel, (int)P.nbt};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 3, 1);
     mark(slot + 4, 0);
-    hipLaunchKernelGGL(scatter_sparse_kernel<E>, dim3(R), dim3(128), 0, st, idx_c, logit_c, mask_c, (int)K, (int)V,
-                       tau, (const int*)count, A.grad_loss, G, P.V_p, Gt, P.R_p, P.fwd ? nullptr : A.status);
-    KD_LAUNCH_CHECK();
+    if (!psel) {
+      hipLaunchKernelGGL(scatter_sparse_kernel<E>, dim3(R), dim3(128), 0, st, idx_c, logit_c, mask_c, (int)K,
+                         (int)V, tau, (const int*)count, A.grad_loss, G, P.V_p, Gt, P.R_p, A.status);
+      KD_LAUNCH_CHECK();
+    }
     mark(slot + 4, 1);
     if (want_dh) {
       mark(slot + 5, 0);
@@ -370,12 +389,25 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       mark(slot + 6, 0);
       const int64_t n = (int64_t)R * d;
       const dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 65536));
-      if (A.gh_dtype == KD_BF16)
-        hipLaunchKernelGGL(dh_reduce_kernel<uint16_t>, grid, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
-                           P.R_p * P.Nd_p, g.splits, R, (int)d, (uint16_t*)A.grad_hidden + c0 * d, d);
-      else
-        hipLaunchKernelGGL(dh_reduce_kernel<float>, grid, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
-                           P.R_p * P.Nd_p, g.splits, R, (int)d, (float*)A.grad_hidden + c0 * d, d);
+      const bool v4 = d % 4 == 0;
+      const dim3 grid4((unsigned)std::min<int64_t>(cdiv(n / 4, 256), 65536));
+      if (A.gh_dtype == KD_BF16) {
+        uint16_t* o = (uint16_t*)A.grad_hidden + c0 * d;
+        if (v4)
+          hipLaunchKernelGGL(dh_reduce4_kernel<uint16_t>, grid4, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
+                             P.R_p * P.Nd_p, g.splits, R, (int)d, o, d);
+        else
+          hipLaunchKernelGGL(dh_reduce_kernel<uint16_t>, grid, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
+                             P.R_p * P.Nd_p, g.splits, R, (int)d, o, d);
+      } else {
+        float* o = (float*)A.grad_hidden + c0 * d;
+        if (v4)
+          hipLaunchKernelGGL(dh_reduce4_kernel<float>, grid4, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
+                             P.R_p * P.Nd_p, g.splits, R, (int)d, o, d);
+        else
+          hipLaunchKernelGGL(dh_reduce_kernel<float>, grid, dim3(256), 0, st, (const float*)dhp, P.Nd_p,
+                             P.R_p * P.Nd_p, g.splits, R, (int)d, o, d);
+      }
       KD_LAUNCH_CHECK();
       mark(slot + 6, 1);
     }
