@@ -68,21 +68,28 @@ struct EpiLsePartial {
     static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
     const int vt = c.m0 / (FM * 32);
     {
+      // the wave's entries, up to 64 per vector load, then one at a time
+      // from registers (no load latency per entry)
       const int b = vt * nbt + c.n0 / kHitT;
-      const int e1 = hit_off[b + 1];
-      for (int e = hit_off[b]; e < e1; ++e) {
-        const uint2 h = hits[e];
-        const int vl = (int)(h.y >> 6), tl = (int)(h.y & 63);
-        const int rr = vl & 31;
-        const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
-        const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
-        float z = 0.f;
+      const int e0 = hit_off[b], n = hit_off[b + 1] - e0;
+      for (int base = 0; base < n; base += 64) {
+        const uint2 hv = base + c.lane < n ? hits[e0 + base + c.lane] : make_uint2(0u, 0u);
+        const int cnt = min(64, n - base);
+        for (int q = 0; q < cnt; ++q) {
+          const uint32_t hx = (uint32_t)__builtin_amdgcn_readlane((int)hv.x, q);
+          const uint32_t hy = (uint32_t)__builtin_amdgcn_readlane((int)hv.y, q);
+          const int vl = (int)(hy >> 6), tl = (int)(hy & 63);
+          const int rr = vl & 31;
+          const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
+          const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
+          float z = 0.f;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            if (i == (vl >> 5) && j == (tl >> 5)) z = acc[i][j][r];
-        if (c.lane == owner) zsel[h.x] = z;
+            for (int j = 0; j < FN; ++j)
+              if (i == (vl >> 5) && j == (tl >> 5)) z = acc[i][j][r];
+          if (c.lane == owner) zsel[hx] = z;
+        }
       }
     }
     const int rows_valid = V - c.m0;          // vocabulary rows of this strip that exist
@@ -186,20 +193,27 @@ struct EpiGrad {
   __device__ __forceinline__ void sparse_part(f32x16 (&acc)[FM][FN], const float (&sc)[FN], const EpiCtx& c) const {
     static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
     const int b = (c.m0 / kHitV) * nbt + c.n0 / kHitT;
-    const int e1 = hit_off[b + 1];
-    for (int e = hit_off[b]; e < e1; ++e) {
-      const uint2 h = hits[e];
-      const int vl = (int)(h.y >> 6), tl = (int)(h.y & 63);
-      const int rr = vl & 31;
-      const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
-      const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
-      const float p = psel[h.x];
-      if (c.lane == owner) {
+    const int e0 = hit_off[b], n = hit_off[b + 1] - e0;
+    for (int base = 0; base < n; base += 64) {
+      // up to 64 entries and their p per vector load, then one at a time
+      const bool in = base + c.lane < n;
+      const uint2 hv = in ? hits[e0 + base + c.lane] : make_uint2(0u, 0u);
+      const float pv = in ? psel[hv.x] : 0.f;
+      const int cnt = min(64, n - base);
+      for (int q = 0; q < cnt; ++q) {
+        const uint32_t hy = (uint32_t)__builtin_amdgcn_readlane((int)hv.y, q);
+        const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), q));
+        const int vl = (int)(hy >> 6), tl = (int)(hy & 63);
+        const int rr = vl & 31;
+        const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
+        const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
+        if (c.lane == owner) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            if (i == (vl >> 5) && j == (tl >> 5)) acc[i][j][r] -= sc[j] * p;
+            for (int j = 0; j < FN; ++j)
+              if (i == (vl >> 5) && j == (tl >> 5)) acc[i][j][r] -= sc[j] * p;
+        }
       }
     }
   }
