@@ -138,6 +138,62 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
+def bench_topk_cache(args, cfg, chunk) -> int:
+    """The offline top-K cache builder (kd_topk_cache_build) on a synthetic
+    teacher head of the workload's shape: T rows of hidden states, d, V, K.
+    Work per row: two passes of the head GEMM, 4*d*V FLOPs."""
+    import numpy as np
+    import torch
+
+    import chunked_top_kl_lm_amd as kd
+    from datagen import make_inputs
+
+    x = make_inputs(cfg, seed=args.seed, topk_backend="torch-cuda")   # its hidden / W serve as the teacher
+    from tests.gpu_util import to_device
+    dev = torch.device("cuda:0")
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    t = to_device(x)
+    H, W = t["hidden"], t["W"]
+    T, d = H.shape
+    V = W.shape[0]
+    K = cfg.K
+    dt = kd.KD_BF16 if x["dtype"] == "bf16" else kd.KD_F32
+    ws = torch.empty(kd.topk_cache_workspace_bytes(T, d, V, K, chunk, dt), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        kd.topk_cache(H, W, K=K, chunk=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        kd.topk_cache(H, W, K=K, chunk=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    flops = 4.0 * T * d * V
+    peak = PEAK_BF16_TFLOPS if dt == kd.KD_BF16 else PEAK_F32_TFLOPS
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {"metric": "tokens/sec top-K teacher-logit cache build (two head-GEMM passes, 4*T*d*V FLOPs)",
+           "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": x["dtype"], "data": "synthetic",
+           "config": {"workload": f"top-K cache of a {cfg.name} head: T={T} d={d} V={V} K={K} chunk={chunk}",
+                      "T": T, "d": d, "V": V, "K": K, "chunk": chunk},
+           "tflops": tflops, "pct_mfma_peak": 100.0 * tflops / peak,
+           "peak_gib": torch.cuda.max_memory_allocated() / 2**30}
+    if not args.no_cpu_baseline:
+        from oracle import topk_cache
+        n = 64
+        t0 = time.perf_counter()
+        topk_cache(x["hidden"][:n], x["W"], K)
+        sec = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n / sec, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+                               "sample": f"first {n} of {T} rows, full d={d} V={V}, fp64 ({sec:.1f} s)"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +207,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 2 GiB device copy (counter calibration)")
+    ap.add_argument("--topk-cache", action="store_true",
+                    help="measure the offline top-K cache builder on the workload's head instead of the loss")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/pmc_traffic.json from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
@@ -174,6 +232,8 @@ def main() -> int:
         over["T"] = args.T
     cfg = config_for(args.workload, **over)
     chunk = args.chunk or cfg.chunk
+    if args.topk_cache:
+        return bench_topk_cache(args, cfg, chunk)
     t_gen = time.perf_counter()
     x = make_inputs(cfg, seed=args.seed, topk_backend="torch-cuda")
     t_gen = time.perf_counter() - t_gen

@@ -12,6 +12,7 @@ import os
 
 __all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
            "fwd", "bwd", "fwd_workspace_bytes", "bwd_workspace_bytes", "KdTopKKLFunction", "kd_topk_kl_loss",
+           "topk_cache", "topk_cache_workspace_bytes",
            "status_str", "STATUS"]
 
 KD_BF16 = 0
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.kd_topk_kl_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, i64,
                                      vp, vp, vp, i32, vp, i32, vp, vp, ctypes.c_size_t, vp, vp]
         L.kd_topk_kl_bwd.restype = i32
+        L.kd_topk_cache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+        L.kd_topk_cache_workspace_bytes.restype = ctypes.c_size_t
+        L.kd_topk_cache_build.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
+        L.kd_topk_cache_build.restype = i32
         L.kd_status_str.argtypes = [i32]
         L.kd_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -158,6 +163,41 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     if row_stats:
         return loss, gH, gW, rl, rk
     return loss, gH, gW
+
+
+def topk_cache_workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> int:
+    return int(lib().kd_topk_cache_workspace_bytes(T, d, V, K, chunk, dtype))
+
+
+def topk_cache(hidden, W, K: int = 100, chunk: int = 2048, workspace=None):
+    """Offline top-K cache of a teacher head (kd_topk_cache_build): returns
+    (idx [T,K] int32, logit [T,K] float32), per row the K largest logits of
+    hidden @ W^T in descending order (equal logits: lower id first)."""
+    import torch
+    T, d = hidden.shape
+    V = W.shape[0]
+    if hidden.dtype == torch.bfloat16:
+        dt = KD_BF16
+    elif hidden.dtype == torch.float32:
+        dt = KD_F32
+    else:
+        raise TypeError("hidden must be bfloat16 or float32")
+    if W.dtype != hidden.dtype or W.shape[1] != d or not (hidden.is_contiguous() and W.is_contiguous()):
+        raise ValueError("hidden [T,d] and W [V,d]: contiguous, same dtype")
+    dev = hidden.device
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    logit = torch.empty((T, K), dtype=torch.float32, device=dev)
+    nbytes = topk_cache_workspace_bytes(T, d, V, K, chunk, dt)
+    if nbytes == 0:
+        raise KdError(2)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kd_topk_cache_build(_ptr(hidden), _ptr(W), dt, T, d, V, K, int(chunk), _ptr(idx), _ptr(logit),
+                                   _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KdError(rc)
+    return idx, logit
 
 
 def fwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chunk: int = 2048,

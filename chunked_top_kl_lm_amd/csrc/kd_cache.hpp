@@ -1,0 +1,237 @@
+// kd_cache.hpp -- kernels of the offline top-K teacher-logit cache builder
+// (gfx950): for every row t of the teacher's final hidden states, the K
+// largest logits z[t, v] = h_t . W_v over the whole vocabulary, with their
+// ids, in descending order (equal logits: lower id first).  The teacher runs
+// once and this record replaces it during training (Glonce, "Multiverse
+// Computing cuts LLM distillation VRAM by 15x with chunked KL loss",
+// paragraph on Multiverse's two-part fix; ainewsbank.com, "Multiverse
+// Computing Tests Lower-Memory Long-Context Distillation", section "Two
+// changes remove different bottlenecks").
+//
+// Per chunk of rows, with the same GEMM as the loss:
+//   pass 1  z^T = W H_c^T; the epilogue keeps, per 32-row vocabulary block
+//           and row, the block's largest logit (EpiBlockMax);
+//   select  per row, the K-th largest of those block maxima: a lower bound
+//           theta_t such that at least K logits are >= theta_t (K of the
+//           blocks have their maximum >= it); radix select on order-
+//           preserving keys (cache_threshold_kernel);
+//   pass 2  the same GEMM again (identical z); the epilogue appends every
+//           z >= theta_t of row t to the row's candidate list (EpiCollect);
+//   sort    per row, the candidates by (z descending, id ascending), the
+//           first K written out (cache_select_kernel).
+// Rows with more candidates than the list holds (many logits tied at or
+// above theta_t) are redone exactly by cache_fallback_kernel, which streams
+// the vocabulary through a sorted top-K in LDS with its own dot products.
+#pragma once
+
+#include "kd_kernels.hpp"
+
+namespace kd {
+
+// Order-preserving unsigned keys of fp32 values (larger float, larger key).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// Sort key of a candidate: z descending, then id ascending, as one uint64
+// (larger = earlier).
+__device__ __forceinline__ uint64_t cand_key(float z, uint32_t id) {
+  return ((uint64_t)fkey(z) << 32) | (uint64_t)(0xffffffffu - id);
+}
+
+constexpr int kBlockRows = 32;   // vocabulary rows per block maximum
+
+// Pass 1: per 32-row vocabulary block and column (row t), the largest logit
+// of the block's valid rows.  out [ceil(V_p/32)][ldp].
+struct EpiBlockMax {
+  float* out;
+  int ldp;
+  int V;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    const int rows_valid = V - c.m0;
+    if (rows_valid <= 0) return;                    // no valid block here (never read)
+    clamp_padding_rows<FM, FN>(acc, rows_valid, c.lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float mx = acc[i][j][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (c.lane < 32 && c.m0 + 32 * i < V) out[(int64_t)(c.m0 / kBlockRows + i) * ldp + c.n0 + 32 * j + c.lane] = mx;
+      }
+  }
+};
+
+// theta_t = the K-th largest of the row's nbv valid block maxima (MSB-first
+// radix select over 8-bit digits of the order-preserving keys), or -inf when
+// there are fewer than K blocks (then every logit is a candidate).  One
+// block of 256 threads per row.
+__global__ __launch_bounds__(256) void cache_threshold_kernel(const float* bmax, int ldp, int nbv, int K,
+                                                              float* theta) {
+  __shared__ int hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_k;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (nbv < K) {
+    if (tid == 0) theta[t] = -INFINITY;
+    return;
+  }
+  uint32_t prefix = 0, mask = 0;
+  int k = K;                                        // rank still to find among the matching keys
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < nbv; i += 256) {
+      const uint32_t key = fkey(bmax[(int64_t)i * ldp + t]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0, dgt = 255;
+      for (; dgt > 0; --dgt) {
+        if (acc + hist[dgt] >= k) break;
+        acc += hist[dgt];
+      }
+      s_prefix = prefix | ((uint32_t)dgt << shift);
+      s_k = k - acc;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    k = s_k;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  if (tid == 0) theta[t] = fkey_inv(prefix);
+}
+
+// Pass 2: every valid z >= theta_t goes to row t's candidate list
+// (cand[t][0, cap), count cnt[t]; appends past cap only count).
+struct EpiCollect {
+  const float* theta;
+  int* cnt;
+  uint2* cand;      // (float bits, id)
+  int cap;
+  int V, R;
+
+  template <int FM, int FN>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = c.n0 + 32 * j + acc_col(c.lane);
+      if (n >= R) continue;
+      const float th = theta[n];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = c.m0 + 32 * i + acc_row(r, c.lane);
+          const float z = acc[i][j][r];
+          if (v < V && z >= th) {
+            const int pos = atomicAdd(&cnt[n], 1);
+            if (pos < cap) cand[(int64_t)n * cap + pos] = make_uint2(__float_as_uint(z), (uint32_t)v);
+          }
+        }
+    }
+  }
+};
+
+// In-LDS bitonic sort of n (a power of two) uint64 keys, descending.
+__device__ __forceinline__ void bitonic_desc(uint64_t* s, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = ((lo & size) == 0);
+        const uint64_t a = s[lo], b = s[hi];
+        if ((a < b) == desc) {
+          s[lo] = b;
+          s[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Per row: sort the candidates, write the first K (ids, logits); rows whose
+// list overflowed are marked for the exact fallback (ovf[t] = 1) and left to
+// it.  cap is a power of two; dynamic LDS holds cap keys.
+__global__ __launch_bounds__(256) void cache_select_kernel(const int* cnt, const uint2* cand, int cap, int K,
+                                                           int32_t* out_idx, float* out_logit, int* ovf) {
+  extern __shared__ uint64_t s_keys[];
+  const int t = blockIdx.x;
+  const int n = cnt[t];
+  if (n > cap) {
+    if (threadIdx.x == 0) ovf[t] = 1;
+    return;
+  }
+  if (threadIdx.x == 0) ovf[t] = 0;
+  int m = 1;
+  while (m < n) m <<= 1;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) {
+    uint64_t key = 0;                               // padding sorts last
+    if (i < n) {
+      const uint2 e = cand[(int64_t)t * cap + i];
+      key = cand_key(__uint_as_float(e.x), e.y);
+    }
+    s_keys[i] = key;
+  }
+  __syncthreads();
+  bitonic_desc(s_keys, m);
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    const uint64_t key = s_keys[k];
+    out_idx[(int64_t)t * K + k] = (int32_t)(0xffffffffu - (uint32_t)key);
+    out_logit[(int64_t)t * K + k] = fkey_inv((uint32_t)(key >> 32));
+  }
+}
+
+// Exact fallback for marked rows: the row's logits recomputed by plain dot
+// products (fp32, summed along d), streamed in batches of kFbBatch ids
+// through a sorted top-K kept in LDS.  Slow (a full pass over W per row);
+// it runs only for rows with more tied candidates than the list holds.
+constexpr int kFbBatch = 1024;
+
+template <class E>
+__global__ __launch_bounds__(256) void cache_fallback_kernel(const typename E::T* H, int64_t ldh,
+                                                             const typename E::T* W, int64_t ldw, int d, int V, int K,
+                                                             int half, const int* ovf, int32_t* out_idx,
+                                                             float* out_logit) {
+  // s_keys: 2 * half keys; [0, half) the best so far (half: a power of two
+  // >= max(K, kFbBatch)), [half, 2 half) the next batch and zero padding
+  extern __shared__ uint64_t s_keys[];
+  const int t = blockIdx.x;
+  if (!ovf[t]) return;
+  const int tot = 2 * half;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) s_keys[i] = 0;
+  const typename E::T* h = H + (int64_t)t * ldh;
+  for (int v0 = 0; v0 < V; v0 += kFbBatch) {
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+      const int v = v0 + i;
+      uint64_t key = 0;
+      if (i < kFbBatch && v < V) {
+        const typename E::T* w = W + (int64_t)v * ldw;
+        float z = 0.f;
+        for (int j = 0; j < d; ++j) z += load_elem<E>(h + j) * load_elem<E>(w + j);
+        key = cand_key(z, (uint32_t)v);
+      }
+      s_keys[half + i] = key;
+    }
+    __syncthreads();
+    bitonic_desc(s_keys, tot);                      // the best `half` move to the front
+  }
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    const uint64_t key = s_keys[k];
+    out_idx[(int64_t)t * K + k] = (int32_t)(0xffffffffu - (uint32_t)key);
+    out_logit[(int64_t)t * K + k] = fkey_inv((uint32_t)(key >> 32));
+  }
+}
+
+}  // namespace kd

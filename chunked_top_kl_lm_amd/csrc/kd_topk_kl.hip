@@ -27,6 +27,7 @@
 #include <string.h>
 
 #include "../../include/kd_topk_kl.h"
+#include "kd_cache.hpp"
 #include "kd_kernels.hpp"
 
 namespace kd {
@@ -459,6 +460,125 @@ size_t workspace_for(int mode, int64_t T, int64_t d, int64_t V, int64_t K, int64
   return p.total;
 }
 
+// ---------------------------------------------------------------------------
+// Offline top-K cache builder (see kd_cache.hpp)
+// ---------------------------------------------------------------------------
+struct CachePlan {
+  int64_t T, d, V, K, chunk, nchunks;
+  int eb;
+  bool pad_d;
+  int64_t d_p, V_p, R_p;
+  int64_t nb32;       // 32-row vocabulary blocks with a valid row
+  int cap;            // candidate list length per row (power of two)
+  int half;           // fallback: power of two >= max(K, batch)
+  size_t off_wp, off_hp, off_bmax, off_theta, off_cnt, off_cand, off_ovf, total;
+};
+
+inline int pow2ceil(int64_t x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+int32_t make_cache_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t dt, CachePlan* p) {
+  if (dt != KD_BF16 && dt != KD_F32) return KD_ERR_DTYPE;
+  if (T < 1 || d < 1 || V < 1 || K < 1 || K > V || K > KD_MAX_K) return KD_ERR_BAD_SHAPE;
+  if (chunk < 1) return KD_ERR_BAD_CHUNK;
+  CachePlan& P = *p;
+  P.T = T; P.d = d; P.V = V; P.K = K;
+  P.chunk = chunk > T ? T : chunk;
+  P.nchunks = cdiv(T, P.chunk);
+  P.eb = dt == KD_BF16 ? 2 : 4;
+  P.pad_d = (d % 64) != 0;
+  P.d_p = round_up(d, 64);
+  P.V_p = round_up(V, kBM);
+  P.R_p = round_up(P.chunk, kBN);
+  if (P.V_p > (1ll << 24) || P.d_p > (1ll << 20) || P.R_p > (1ll << 20) || T > (1ll << 31) / 2)
+    return KD_ERR_BAD_SHAPE;
+  if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_p * P.eb >= (1ll << 32))
+    return KD_ERR_BAD_SHAPE;
+  P.nb32 = cdiv(V, kBlockRows);
+  // Candidate list: twice K (rounded up to a power of two), at least 256;
+  // when there are fewer blocks than K every logit is a candidate, so the
+  // list must hold V.  Past 8192 (64 KB of sort keys) rows go to the
+  // fallback.
+  int64_t want = std::max<int64_t>(2 * K, 256);
+  if (P.nb32 < K) want = std::max<int64_t>(want, V);
+  P.cap = pow2ceil(std::min<int64_t>(want, 8192));
+  P.half = pow2ceil(std::max<int64_t>(K, kFbBatch));
+  const size_t e = (size_t)P.eb;
+  size_t o = 0;
+  P.off_wp = o; if (P.pad_d) o = align256(o + (size_t)V * P.d_p * e);
+  P.off_hp = o; if (P.pad_d) o = align256(o + (size_t)P.R_p * P.d_p * e);
+  P.off_bmax = o; o = align256(o + (size_t)(P.V_p / kBlockRows) * P.R_p * sizeof(float));
+  P.off_theta = o; o = align256(o + (size_t)P.R_p * sizeof(float));
+  P.off_cnt = o; o = align256(o + (size_t)P.R_p * sizeof(int));
+  P.off_cand = o; o = align256(o + (size_t)P.R_p * P.cap * sizeof(uint2));
+  P.off_ovf = o; o = align256(o + (size_t)P.R_p * sizeof(int));
+  P.total = o;
+  return KD_OK;
+}
+
+template <class E>
+int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t* out_idx, float* out_logit, char* ws,
+                  hipStream_t st) {
+  typedef typename E::T T;
+  T* Wp = (T*)(ws + P.off_wp);
+  T* Hp = (T*)(ws + P.off_hp);
+  float* bmax = (float*)(ws + P.off_bmax);
+  float* theta = (float*)(ws + P.off_theta);
+  int* cnt = (int*)(ws + P.off_cnt);
+  uint2* cand = (uint2*)(ws + P.off_cand);
+  int* ovf = (int*)(ws + P.off_ovf);
+  const int64_t d = P.d, V = P.V, K = P.K;
+
+  const T* Wsrc = (const T*)W;
+  int64_t ldw = d;
+  if (P.pad_d) {
+    const int64_t n = V * P.d_p;
+    hipLaunchKernelGGL(pad_kernel<E>, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
+                       (const T*)W, d, V, d, Wp, P.d_p, V);
+    KD_LAUNCH_CHECK();
+    Wsrc = Wp;
+    ldw = P.d_p;
+  }
+  const int64_t kbytes_d = P.d_p * P.eb;
+  for (int64_t c = 0; c < P.nchunks; ++c) {
+    const int64_t c0 = c * P.chunk;
+    const int R = (int)std::min<int64_t>(P.chunk, P.T - c0);
+    const T* Hc = (const T*)hidden + c0 * d;
+    const T* Hsrc = Hc;
+    int64_t ldh = d;
+    if (P.pad_d) {
+      const int64_t Rt = round_up(R, kBN);
+      const int64_t n = Rt * P.d_p;
+      hipLaunchKernelGGL(pad_kernel<E>, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
+                         Hc, d, (int64_t)R, d, Hp, P.d_p, Rt);
+      KD_LAUNCH_CHECK();
+      Hsrc = Hp;
+      ldh = P.d_p;
+    }
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)cdiv(R, 256)), dim3(256), 0, st, cnt, (int64_t)R, 0);
+    KD_LAUNCH_CHECK();
+    GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
+    if (launch_gemm<TileMain, E>(g, EpiBlockMax{bmax, (int)P.R_p, (int)V}, st) != hipSuccess) return KD_ERR_HIP;
+    hipLaunchKernelGGL(cache_threshold_kernel, dim3(R), dim3(256), 0, st, (const float*)bmax, (int)P.R_p,
+                       (int)P.nb32, (int)K, theta);
+    KD_LAUNCH_CHECK();
+    if (launch_gemm<TileMain, E>(g, EpiCollect{theta, cnt, cand, P.cap, (int)V, R}, st) != hipSuccess)
+      return KD_ERR_HIP;
+    int32_t* oi = out_idx + c0 * K;
+    float* ol = out_logit + c0 * K;
+    hipLaunchKernelGGL(cache_select_kernel, dim3(R), dim3(256), (size_t)P.cap * sizeof(uint64_t), st,
+                       (const int*)cnt, (const uint2*)cand, P.cap, (int)K, oi, ol, ovf);
+    KD_LAUNCH_CHECK();
+    hipLaunchKernelGGL(cache_fallback_kernel<E>, dim3(R), dim3(256), (size_t)2 * P.half * sizeof(uint64_t), st, Hc,
+                       d, (const T*)W, d, (int)d, (int)V, (int)K, P.half, (const int*)ovf, oi, ol);
+    KD_LAUNCH_CHECK();
+  }
+  return KD_OK;
+}
+
 }  // namespace
 }  // namespace kd
 
@@ -529,6 +649,26 @@ int32_t kd_topk_kl_bwd(const void* hidden, const void* W, int32_t in_dtype, cons
              grad_loss, grad_hidden, grad_hidden_dtype, grad_W, accumulate_grad_W ? 1 : 0, grad_W_bf16, status_dev,
              (hipStream_t)stream, nullptr};
   return kd::dispatch(kd::kBackward, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
+}
+
+size_t kd_topk_cache_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
+  kd::CachePlan p;
+  if (kd::make_cache_plan(T, d, V, K, chunk, in_dtype, &p) != KD_OK) return 0;
+  return p.total;
+}
+
+int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype, int64_t T, int64_t d, int64_t V,
+                            int64_t K, int64_t chunk, int32_t* out_idx, float* out_logit, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!hidden || !W || !out_idx || !out_logit) return KD_ERR_NULL_ARG;
+  kd::CachePlan p;
+  const int32_t st = kd::make_cache_plan(T, d, V, K, chunk, in_dtype, &p);
+  if (st != KD_OK) return st;
+  if ((((uintptr_t)hidden) | ((uintptr_t)W)) & 15) return KD_ERR_BAD_SHAPE;
+  if (!workspace || workspace_bytes < p.total || (((uintptr_t)workspace) & 255)) return KD_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (in_dtype == KD_BF16) return kd::run_cache<kd::Bf16>(p, hidden, W, out_idx, out_logit, (char*)workspace, s);
+  return kd::run_cache<kd::F32>(p, hidden, W, out_idx, out_logit, (char*)workspace, s);
 }
 
 const char* kd_status_str(int32_t s) {

@@ -210,6 +210,37 @@ int32_t kd_topk_kl_bwd(const void* hidden, const void* W, int32_t in_dtype,
                        void* workspace, size_t workspace_bytes,
                        int32_t* status_dev, void* stream);
 
+/*
+ * Offline top-K teacher-logit cache: the record the loss reads as
+ * teacher_idx / teacher_logit.  The teacher runs once ahead of training and
+ * its K largest output logits per position are stored with their token ids
+ * (Glonce, "Multiverse Computing cuts LLM distillation VRAM by 15x with
+ * chunked KL loss", paragraph on Multiverse's two-part fix: K = 100;
+ * ainewsbank.com, "Multiverse Computing Tests Lower-Memory Long-Context
+ * Distillation", section "Two changes remove different bottlenecks").
+ *
+ *  hidden     device [T, d] in_dtype: the teacher's final hidden states.
+ *  W          device [V, d] in_dtype: the teacher's output head.
+ *  out_idx    device [T, K] int32 (written): per row the ids of the K largest
+ *             logits z[t, v] = h_t . W_v, in descending order of z; equal
+ *             logits are ordered by the lower id.
+ *  out_logit  device [T, K] float32 (written): those logits.
+ *  chunk      rows processed at a time (the logits of a chunk are computed
+ *             twice and never stored).
+ * Workspace: kd_topk_cache_workspace_bytes(...) bytes, 256-byte aligned;
+ * O(chunk * (V / 32 + K)), independent of T beyond the chunk.  Host errors
+ * as for kd_topk_kl_fwd_bwd.  Logits are fp32 sums of exact bf16 (or fp32)
+ * products; rows where more than about 2K logits tie at or above the
+ * selection threshold are recomputed by a slower exact path with plain dot
+ * products.
+ */
+size_t kd_topk_cache_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K,
+                                     int64_t chunk, int32_t in_dtype);
+int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype,
+                            int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                            int32_t* out_idx, float* out_logit,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kd_status_str(int32_t status);
 

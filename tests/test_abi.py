@@ -22,7 +22,8 @@ def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {"kd_topk_kl_workspace_bytes", "kd_topk_kl_fwd_bwd",
                                           "kd_topk_kl_fwd_bwd_timed", "kd_status_str",
                                           "kd_topk_kl_fwd_workspace_bytes", "kd_topk_kl_bwd_workspace_bytes",
-                                          "kd_topk_kl_fwd", "kd_topk_kl_bwd"}
+                                          "kd_topk_kl_fwd", "kd_topk_kl_bwd",
+                                          "kd_topk_cache_workspace_bytes", "kd_topk_cache_build"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -144,3 +145,26 @@ def test_fwd_host_argument_errors(kw, code):
 ])
 def test_bwd_host_argument_errors(kw, code):
     assert _call_bwd(**kw) == code
+
+
+def test_topk_cache_host_checks():
+    wb = kd.topk_cache_workspace_bytes
+    assert wb(0, 8, 8, 1, 1, 0) == 0 and wb(8, 8, 8, 9, 1, 0) == 0 and wb(8, 8, 8, 1, 1, 5) == 0
+    a, b = wb(32768, 2880, 201088, 100, 2048, 0), wb(262144, 2880, 201088, 100, 2048, 0)
+    assert a == b > 0 and a < 64 * 2**20
+
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=None), 1), (dict(W=None), 1), (dict(idx=None), 1), (dict(logit=None), 1),
+    (dict(K=0), 2), (dict(K=1001), 2), (dict(T=0), 2), (dict(chunk=0), 4), (dict(dt=4), 5),
+    (dict(ws=None), 6), (dict(wsb=100), 6), (dict(hidden=0x10004), 2),
+])
+def test_topk_cache_host_argument_errors(kw, code):
+    # every case fails in host validation, before any HIP call
+    a = dict(hidden=0x10000, W=0x20000, dt=0, T=64, d=64, V=1000, K=10, chunk=32, idx=0x30000, logit=0x40000,
+             ws=0x100000, wsb=1 << 40)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    assert kd.lib().kd_topk_cache_build(v(a["hidden"]), v(a["W"]), a["dt"], a["T"], a["d"], a["V"], a["K"],
+                                        a["chunk"], v(a["idx"]), v(a["logit"]), v(a["ws"]), a["wsb"], None) == code
