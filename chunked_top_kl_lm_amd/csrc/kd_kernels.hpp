@@ -61,7 +61,7 @@ struct EpiLsePartial {
   const int* hit_off;   // [nvt * nbt + 1] start of each wave tile's hit list
   const uint2* hits;    // (slot t*K + k, (v % kHitV) << 6 | (t % kHitT))
   float* zsel;          // [R * K] z at the teacher ids
-  int nbt;              // row groups of kHitT in the chunk
+  int hstride;          // offsets per row group: strips + 1
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
@@ -70,7 +70,7 @@ struct EpiLsePartial {
     {
       // the wave's entries, up to 64 per vector load, then one at a time
       // from registers (no load latency per entry)
-      const int b = vt * nbt + c.n0 / kHitT;
+      const int b = (c.n0 / kHitT) * hstride + vt;
       const int e0 = hit_off[b], n = hit_off[b + 1] - e0;
       for (int base = 0; base < n; base += 64) {
         const uint2 hv = base + c.lane < n ? hits[e0 + base + c.lane] : make_uint2(0u, 0u);
@@ -150,7 +150,7 @@ struct EpiGrad {
   const int* hit_off;
   const uint2* hits;
   const float* psel;
-  int nbt;
+  int hstride;
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
@@ -192,7 +192,7 @@ struct EpiGrad {
   template <int FM, int FN>
   __device__ __forceinline__ void sparse_part(f32x16 (&acc)[FM][FN], const float (&sc)[FN], const EpiCtx& c) const {
     static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
-    const int b = (c.m0 / kHitV) * nbt + c.n0 / kHitT;
+    const int b = (c.n0 / kHitT) * hstride + c.m0 / kHitV;
     const int e0 = hit_off[b], n = hit_off[b + 1] - e0;
     for (int base = 0; base < n; base += 64) {
       // up to 64 entries and their p per vector load, then one at a time
@@ -470,93 +470,72 @@ __global__ __launch_bounds__(1024) void prep_kernel(const uint8_t* mask, int64_t
   }
 }
 
-// Teacher-id hit lists of a chunk, filed by forward-GEMM wave tile
-// (vocabulary strip id / kHitV, row group t / kHitT): a counting sort in
-// three launches -- count, scan (which also clears the counts for the next
-// chunk), fill.  Entries of one list come in any order; each names its own
-// output slot, so the results do not depend on it.
+// Teacher-id hit lists of a chunk, filed by forward-GEMM wave tile: one
+// block per 64-row group g of the chunk sorts the group's (t, k) entries by
+// vocabulary strip id / kHitV (counting sort in LDS: count, scan, fill).
+// Group g owns the fixed range [g 64 K, (g + 1) 64 K) of `hits`, so no
+// global scan is needed; off[g (nvt + 1) + vt] is where strip vt's list
+// starts, off[g (nvt + 1) + vt + 1] where it ends.  Entries of one list come
+// in any order; each names its own output slot, so results do not depend on
+// it.  Groups past the chunk's rows (up to the GEMM tiles' extent) get empty
+// lists.  Dynamic LDS: nvt + 1 ints.
 __global__ __launch_bounds__(256) void fill_i32_kernel(int* p, int64_t n, int v) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
-__global__ __launch_bounds__(256) void hit_count_kernel(const int32_t* idx, int R, int K, int V, int nbt,
-                                                        int* cnt) {
-  const int64_t n = (int64_t)R * K;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int id = idx[i];
-    if (id < 0 || id >= V) continue;
-    const int t = (int)(i / K);
-    atomicAdd(&cnt[(id / kHitV) * nbt + t / kHitT], 1);
-  }
-}
-
-// Exclusive scan of the counts into off (and cur, the fill cursors); the
-// counts are cleared for the next chunk.  One block; each pass covers
-// kScanTile counts, 16 contiguous per thread (vector loads, serial scan in
-// registers, wave scan with shuffles, wave totals through LDS).  The arrays
-// are padded to a multiple of kScanTile; padding counts stay zero.
-constexpr int kScanPer = 16;
-constexpr int kScanTile = 1024 * kScanPer;
-
-__global__ __launch_bounds__(1024) void hit_scan_kernel(int* cnt, int nb_p, int* off, int* cur, int nb) {
+__global__ __launch_bounds__(1024) void hit_build_kernel(const int32_t* idx, int R, int K, int V, int nvt, int* off,
+                                                         uint2* hits) {
+  extern __shared__ int s_h[];
   __shared__ int s_w[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int carry = 0;
-  for (int base = 0; base < nb_p; base += kScanTile) {
-    int4* pc = (int4*)(cnt + base + tid * kScanPer);
-    int x[kScanPer];
-#pragma unroll
-    for (int q = 0; q < kScanPer / 4; ++q) {
-      const int4 v = pc[q];
-      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
-    }
-    int tsum = 0;
-#pragma unroll
-    for (int q = 0; q < kScanPer; ++q) {   // exclusive within the thread
-      const int c = x[q];
-      x[q] = tsum;
-      tsum += c;
-    }
-    int incl = tsum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) s_w[w] = incl;
-    __syncthreads();
-    int wpre = 0, total = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int sw = s_w[i];
-      wpre += i < w ? sw : 0;
-      total += sw;
-    }
-    const int ex = carry + wpre + incl - tsum;
-    int4* po = (int4*)(off + base + tid * kScanPer);
-    int4* pu = (int4*)(cur + base + tid * kScanPer);
-#pragma unroll
-    for (int q = 0; q < kScanPer / 4; ++q) {
-      const int4 v = make_int4(ex + x[4 * q], ex + x[4 * q + 1], ex + x[4 * q + 2], ex + x[4 * q + 3]);
-      po[q] = v;
-      pu[q] = v;
-      pc[q] = make_int4(0, 0, 0, 0);
-    }
-    carry += total;
-    __syncthreads();                          // s_w is reused by the next pass
+  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t0 = g * kHitT;
+  const int rows = max(0, min(kHitT, R - t0));
+  const int n = rows * K;
+  const int base = t0 * K;
+  const int32_t* ids = idx + (int64_t)t0 * K;
+  for (int i = tid; i <= nvt; i += 1024) s_h[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < n; e += 1024) {
+    const int id = ids[e];
+    if (id >= 0 && id < V) atomicAdd(&s_h[id / kHitV], 1);
   }
-  if (tid == 0) off[nb] = carry;
-}
-
-__global__ __launch_bounds__(256) void hit_fill_kernel(const int32_t* idx, int R, int K, int V, int nbt, int* cur,
-                                                       uint2* hits) {
-  const int64_t n = (int64_t)R * K;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int id = idx[i];
+  __syncthreads();
+  // exclusive scan of s_h[0, nvt): contiguous pieces per thread, wave scan
+  // of the piece sums, wave totals through LDS
+  const int per = (nvt + 1023) / 1024;
+  const int a = min(nvt, tid * per), b = min(nvt, a + per);
+  int sum = 0;
+  for (int i = a; i < b; ++i) sum += s_h[i];
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_w[w] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    run += i < w ? s_w[i] : 0;
+    total += s_w[i];
+  }
+  for (int i = a; i < b; ++i) {
+    const int c = s_h[i];
+    s_h[i] = run;
+    run += c;
+  }
+  __syncthreads();
+  int* o = off + (int64_t)g * (nvt + 1);
+  for (int i = tid; i < nvt; i += 1024) o[i] = base + s_h[i];
+  if (tid == 0) o[nvt] = base + total;
+  __syncthreads();
+  for (int e = tid; e < n; e += 1024) {
+    const int id = ids[e];
     if (id < 0 || id >= V) continue;
-    const int t = (int)(i / K);
-    const int p = atomicAdd(&cur[(id / kHitV) * nbt + t / kHitT], 1);
-    hits[p] = make_uint2((uint32_t)i, (uint32_t)(((id % kHitV) << 6) | (t % kHitT)));
+    const int pos = base + atomicAdd(&s_h[id / kHitV], 1);
+    const int t = e / K;                             // row within the group
+    hits[pos] = make_uint2((uint32_t)(base + e), (uint32_t)(((id % kHitV) << 6) | t));
   }
 }
 

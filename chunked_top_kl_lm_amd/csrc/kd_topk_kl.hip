@@ -76,12 +76,11 @@ struct Plan {
   int dh_bn, dw_bn;   // column tile (over d) of the hidden- and head-gradient GEMMs
   int64_t nvt;        // LSE strips per row
   int splits;         // split-K factor of the hidden-gradient GEMM
-  int64_t nbt, nhb;   // teacher-id hit lists: row groups per chunk, lists per chunk
-  int64_t nhb_p;      // nhb padded for the scan
+  int64_t nbt;        // teacher-id hit lists: row groups per chunk
   int64_t ng;         // first-level LSE merge groups per row
   // workspace offsets (buffers a mode does not use take no space)
   size_t off_scalar, off_wt, off_wp, off_hp, off_ht, off_g, off_gt, off_part, off_lse2, off_rowkl, off_dh;
-  size_t off_hcnt, off_hoff, off_hcur, off_hits, off_zsel, off_part2, off_psel;
+  size_t off_hoff, off_hits, off_zsel, off_part2, off_psel;
   size_t total;
 };
 
@@ -106,8 +105,6 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.Nd_p = round_up(d, P.dh_bn);
   P.nvt = P.V_p / kWaveM;
   P.nbt = P.R_p / kHitT;
-  P.nhb = P.nvt * P.nbt;
-  P.nhb_p = round_up(P.nhb, kScanTile);
   P.ng = cdiv(P.nvt, kMergeStrips);
   // Addressing limits: per-tile buffer ranges and int32 tile indices.
   if (P.V_p > (1ll << 24) || P.d_p > (1ll << 20) || P.R_p > (1ll << 20) || T > (1ll << 31) / 2)
@@ -115,7 +112,8 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_p * P.eb >= (1ll << 32))
     return KD_ERR_BAD_SHAPE;
   // hit-list entries are int32-indexed
-  if (P.R_p * K >= (1ll << 31) || P.nhb_p >= (1ll << 28)) return KD_ERR_BAD_SHAPE;
+  // hit lists: int32 entry indices; a row group's strip counts sit in LDS
+  if (P.R_p * K >= (1ll << 31) || (P.nvt + 1) * 4 > 65536) return KD_ERR_BAD_SHAPE;
   // split-K of the hidden-gradient GEMM (output only chunk x d): pick the
   // split count whose grid fills whole waves of 256 CUs best, with at least
   // one full wave, and a small penalty per split for the partial-sum traffic.
@@ -153,9 +151,7 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   take(P.off_lse2, F, (size_t)P.R_p * sizeof(float));
   take(P.off_rowkl, F, (size_t)P.R_p * sizeof(double));
   take(P.off_dh, B, (size_t)P.splits * P.R_p * P.Nd_p * sizeof(float));
-  take(P.off_hcnt, F, (size_t)P.nhb_p * sizeof(int));
-  take(P.off_hoff, F, (size_t)(P.nhb_p + 1) * sizeof(int));
-  take(P.off_hcur, F, (size_t)P.nhb_p * sizeof(int));
+  take(P.off_hoff, F, (size_t)P.nbt * (P.nvt + 1) * sizeof(int));
   take(P.off_hits, F, (size_t)P.R_p * K * sizeof(uint2));
   take(P.off_zsel, F, (size_t)P.R_p * K * sizeof(float));
   take(P.off_part2, F, (size_t)P.ng * P.R_p * sizeof(float2));
@@ -253,9 +249,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
   float* lse2 = (float*)(ws + P.off_lse2);
   double* rowkl = (double*)(ws + P.off_rowkl);
   float* dhp = (float*)(ws + P.off_dh);
-  int* hcnt = (int*)(ws + P.off_hcnt);
   int* hoff = (int*)(ws + P.off_hoff);
-  int* hcur = (int*)(ws + P.off_hcur);
   uint2* hits = (uint2*)(ws + P.off_hits);
   float* zsel = (float*)(ws + P.off_zsel);
   float2* part2 = (float2*)(ws + P.off_part2);
@@ -269,11 +263,6 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
   mark(pro_slot, 0);
   hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(1024), 0, st, A.mask, T_, count, loss_acc, A.status);
   KD_LAUNCH_CHECK();
-  if (P.fwd) {
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(P.nhb_p, 256), 4096)), dim3(256), 0,
-                       st, hcnt, P.nhb_p, 0);
-    KD_LAUNCH_CHECK();
-  }
   if (want_dh) {
     // W^T, zero-padded to [d_p][V_p]
     launch_transpose<E>((const T*)A.W, d, V, d, Wt, P.V_p, (unsigned)(P.V_p / 64), (unsigned)(P.d_p / 64), st);
@@ -319,13 +308,8 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
     }
     if (P.fwd) {
       // teacher-id hit lists for the forward epilogue
-      const unsigned nblk = (unsigned)std::min<int64_t>(cdiv((int64_t)R * K, 256), 4096);
-      hipLaunchKernelGGL(hit_count_kernel, dim3(nblk), dim3(256), 0, st, idx_c, R, (int)K, (int)V, (int)P.nbt, hcnt);
-      KD_LAUNCH_CHECK();
-      hipLaunchKernelGGL(hit_scan_kernel, dim3(1), dim3(1024), 0, st, hcnt, (int)P.nhb_p, hoff, hcur, (int)P.nhb);
-      KD_LAUNCH_CHECK();
-      hipLaunchKernelGGL(hit_fill_kernel, dim3(nblk), dim3(256), 0, st, idx_c, R, (int)K, (int)V, (int)P.nbt, hcur,
-                         hits);
+      hipLaunchKernelGGL(hit_build_kernel, dim3((unsigned)(Rt / kHitT)), dim3(1024),
+                         (size_t)(P.nvt + 1) * sizeof(int), st, idx_c, R, (int)K, (int)V, (int)P.nvt, hoff, hits);
       KD_LAUNCH_CHECK();
     }
     mark(slot + 0, 1);
@@ -335,7 +319,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       mark(slot + 1, 0);
       {
         GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-        EpiLsePartial epi{part, (int)P.R_p, (int)V, c2, hoff, hits, zsel, (int)P.nbt};
+        EpiLsePartial epi{part, (int)P.R_p, (int)V, c2, hoff, hits, zsel, (int)(P.nvt + 1)};
         if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
       }
       mark(slot + 1, 1);
@@ -363,7 +347,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
       // fused call: the sparse teacher part goes in the epilogue
       EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse_src, lse_to2, mask_c, count, A.grad_loss, tau, c2, (int)V, R,
-                     psel ? hoff : nullptr, hits, psel, (int)P.nbt};
+                     psel ? hoff : nullptr, hits, psel, (int)(P.nvt + 1)};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 3, 1);
