@@ -51,8 +51,9 @@ extern "C" {
 /* Status codes. */
 #define KD_OK 0
 #define KD_ERR_NULL_ARG 1    /* a required pointer is NULL                      */
-#define KD_ERR_BAD_SHAPE 2   /* T, d, V or K < 1, K > V, K > KD_MAX_K, or V*d,  */
-                             /* chunk*V or T*d exceeds what the kernels address */
+#define KD_ERR_BAD_SHAPE 2   /* T, d, V or K < 1, K > V, K > KD_MAX_K, V*d,     */
+                             /* chunk*V or T*d beyond what the kernels address, */
+                             /* or (loss, forward) V > 2097024                  */
 #define KD_ERR_BAD_TAU 3     /* tau <= 0 or not finite                          */
 #define KD_ERR_BAD_CHUNK 4   /* chunk < 1                                       */
 #define KD_ERR_DTYPE 5       /* in_dtype is not KD_BF16 or KD_F32               */
