@@ -301,10 +301,13 @@ def main() -> int:
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if dt == kd.KD_BF16 else PEAK_F32_TFLOPS
     dom = max(GEMM_PHASES, key=lambda k: phase_ms[k])
-    launch_ms = phase_ms[dom] / nchunks
-    # algorithmic work per launch: 2*d*V FLOPs per token, R = chunk tokens per launch
-    # (average over launches; the last chunk may be ragged)
-    alg_flops = 2.0 * d * V * T / nchunks
+    # launches per step: one per chunk, except the head-gradient GEMM, which
+    # contracts dw_chunks consecutive chunks per launch
+    launches = -(-nchunks // kd.dw_chunks(T, d, V, K, chunk, dt)) if dom == "gemm_dW" else nchunks
+    launch_ms = phase_ms[dom] / launches
+    # algorithmic work per launch: 2*d*V FLOPs per token over the T tokens of
+    # a step (average over launches; the last chunk may be ragged)
+    alg_flops = 2.0 * d * V * T / launches
     achieved = alg_flops / (launch_ms * 1e-3) / 1e12
     traffic, traffic_detail = load_traffic(dom)
 

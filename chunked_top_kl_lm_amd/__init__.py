@@ -11,8 +11,8 @@ import ctypes
 import os
 
 __all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
-           "fwd", "bwd", "fwd_workspace_bytes", "bwd_workspace_bytes", "KdTopKKLFunction", "kd_topk_kl_loss",
-           "topk_cache", "topk_cache_workspace_bytes",
+           "fwd", "bwd", "fwd_workspace_bytes", "bwd_workspace_bytes", "dw_chunks", "KdTopKKLFunction",
+           "kd_topk_kl_loss", "topk_cache", "topk_cache_workspace_bytes",
            "status_str", "STATUS"]
 
 KD_BF16 = 0
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.kd_topk_kl_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.kd_topk_kl_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
         L.kd_topk_kl_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.kd_topk_kl_dw_chunks.argtypes = [i64, i64, i64, i64, i64, i32]
+        L.kd_topk_kl_dw_chunks.restype = i32
         L.kd_topk_kl_fwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, i64,
                                      vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.kd_topk_kl_fwd.restype = i32
@@ -84,6 +86,11 @@ def fwd_workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype: int) 
 
 def bwd_workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> int:
     return int(lib().kd_topk_kl_bwd_workspace_bytes(T, d, V, K, chunk, dtype))
+
+
+def dw_chunks(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> int:
+    """Chunks contracted by one launch of the head-gradient GEMM (0: invalid sizes)."""
+    return int(lib().kd_topk_kl_dw_chunks(T, d, V, K, chunk, dtype))
 
 
 def _ptr(t):

@@ -56,6 +56,12 @@ using TileHeadNarrow = TileCfg<256, 128, 4, 2, 2, 128>;
 constexpr int kBM = TileMain::BM, kBN = TileMain::BN;
 constexpr int kWaveM = TileMain::BM / TileMain::WM;   // vocabulary strip of one LSE partial
 constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
+// The head-gradient GEMM contracts over at least this many rows per launch
+// (several consecutive chunks when the chunk is smaller): each launch reads
+// and writes the whole fp32 grad_W once, so fewer, longer launches halve
+// that traffic at 2048-row chunks (2.19 vs 2.44 ms per 2048 rows at
+// d = 2880, V = 201088) for one more chunk-sized G^T buffer.
+constexpr int64_t kDwRows = 4096;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -74,6 +80,8 @@ struct Plan {
   bool pad_d;         // d is not a multiple of 64: use zero-padded copies
   int64_t d_p, V_p, R_p, Nd_p;
   int dh_bn, dw_bn;   // column tile (over d) of the hidden- and head-gradient GEMMs
+  int dw_group;       // consecutive chunks whose G^T and H_c^T one head-gradient GEMM contracts
+  int64_t R_g;        // dw_group * R_p: row stride of the G^T and H_c^T buffers
   int64_t nvt;        // LSE strips per row
   int splits;         // split-K factor of the hidden-gradient GEMM
   int64_t nbt;        // teacher-id hit lists: row groups per chunk
@@ -104,12 +112,14 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.dw_bn = round_up(d, TileHead::BN) <= round_up(d, TileHeadNarrow::BN) ? TileHead::BN : TileHeadNarrow::BN;
   P.Nd_p = round_up(d, P.dh_bn);
   P.nvt = P.V_p / kWaveM;
+  P.dw_group = P.bwd ? (int)std::max<int64_t>(1, std::min<int64_t>(P.nchunks, kDwRows / P.R_p)) : 1;
+  P.R_g = P.dw_group * P.R_p;
   P.nbt = P.R_p / kHitT;
   P.ng = cdiv(P.nvt, kMergeStrips);
   // Addressing limits: per-tile buffer ranges and int32 tile indices.
-  if (P.V_p > (1ll << 24) || P.d_p > (1ll << 20) || P.R_p > (1ll << 20) || T > (1ll << 31) / 2)
+  if (P.V_p > (1ll << 24) || P.d_p > (1ll << 20) || P.R_g > (1ll << 20) || T > (1ll << 31) / 2)
     return KD_ERR_BAD_SHAPE;
-  if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_p * P.eb >= (1ll << 32))
+  if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_g * P.eb >= (1ll << 32))
     return KD_ERR_BAD_SHAPE;
   // hit-list entries are int32-indexed
   // hit lists: int32 entry indices; a row group's strip counts sit in LDS
@@ -144,9 +154,9 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   take(P.off_wt, B, (size_t)P.d_p * P.V_p * e);
   take(P.off_wp, P.pad_d, (size_t)V * P.d_p * e);
   take(P.off_hp, P.pad_d, (size_t)P.R_p * P.d_p * e);
-  take(P.off_ht, B, (size_t)P.d_p * P.R_p * e);
+  take(P.off_ht, B, (size_t)P.d_p * P.R_g * e);
   take(P.off_g, B, (size_t)P.R_p * P.V_p * e);
-  take(P.off_gt, B, (size_t)P.V_p * P.R_p * e);
+  take(P.off_gt, B, (size_t)P.V_p * P.R_g * e);
   take(P.off_part, F, (size_t)P.nvt * P.R_p * sizeof(float2));
   take(P.off_lse2, F, (size_t)P.R_p * sizeof(float));
   take(P.off_rowkl, F, (size_t)P.R_p * sizeof(double));
@@ -286,6 +296,10 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
     const int R = (int)std::min<int64_t>(P.chunk, T_ - c0);
     const int64_t Rt = round_up(R, kBN);     // rows covered by the GEMM tiles this chunk
     const int64_t slot = c * KD_NUM_PHASES;
+    // the chunk's column slot in G^T / H_c^T; the head-gradient GEMM runs
+    // once per group of dw_group chunks, over all of the group's rows
+    const int64_t gslot = c % P.dw_group;
+    const bool group_end = gslot == P.dw_group - 1 || c == P.nchunks - 1;
     const uint8_t* mask_c = A.mask ? A.mask + c0 : nullptr;
     const int32_t* idx_c = A.idx + c0 * K;
     const float* logit_c = A.logit + c0 * K;
@@ -302,8 +316,9 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       ldh = P.d_p;
     }
     if (want_dw) {
-      // H_c^T, zero-padded to [d_p][R_p]
-      launch_transpose<E>(Hc, d, (int64_t)R, d, Ht, P.R_p, (unsigned)(P.R_p / 64), (unsigned)(P.d_p / 64), st);
+      // H_c^T, zero-padded to [d_p][R_p], into the chunk's slot of the group
+      launch_transpose<E>(Hc, d, (int64_t)R, d, Ht + gslot * P.R_p, P.R_g, (unsigned)(P.R_p / 64),
+                          (unsigned)(P.d_p / 64), st);
       KD_LAUNCH_CHECK();
     }
     if (P.fwd) {
@@ -346,7 +361,8 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       const float lse_to2 = P.fwd ? 1.f : kLog2e;
       GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
       // fused call: the sparse teacher part goes in the epilogue
-      EpiGrad<E> epi{G, P.V_p, Gt, P.R_p, lse_src, lse_to2, mask_c, count, A.grad_loss, tau, c2, (int)V, R,
+      EpiGrad<E> epi{G, P.V_p, Gt + gslot * P.R_p, P.R_g, lse_src, lse_to2, mask_c, count, A.grad_loss, tau, c2,
+                     (int)V, R,
                      psel ? hoff : nullptr, hits, psel, (int)(P.nvt + 1)};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
@@ -354,7 +370,8 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
     mark(slot + 4, 0);
     if (!psel) {
       hipLaunchKernelGGL(scatter_sparse_kernel<E>, dim3(R), dim3(128), 0, st, idx_c, logit_c, mask_c, (int)K,
-                         (int)V, tau, (const int*)count, A.grad_loss, G, P.V_p, Gt, P.R_p, A.status);
+                         (int)V, tau, (const int*)count, A.grad_loss, G, P.V_p, Gt + gslot * P.R_p, P.R_g,
+                         A.status);
       KD_LAUNCH_CHECK();
     }
     mark(slot + 4, 1);
@@ -398,14 +415,19 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
     }
     if (want_dw) {
       mark(slot + 7, 0);
-      // dW (+)= G^T H_c  (A = G^T [V_p x R_p], B = H_c^T [d x R_p])
-      EpiAccum epi{A.grad_W, d, (int)V, (int)d, (c == 0 && !A.accumulate_W) ? 1 : 0};
-      if (P.dw_bn == TileHead::BN) {
-        GemmShape g = make_shape<TileHead>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
-        if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
-      } else {
-        GemmShape g = make_shape<TileHeadNarrow>(Gt, P.R_p, (int)V, Ht, P.R_p, (int)d, Rt * P.eb, 1, 4);
-        if (launch_gemm<TileHeadNarrow, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+      if (group_end) {
+        // dW (+)= G^T H^T over the group's rows (A = G^T [V_p x R_g], B =
+        // H^T [d x R_g]); a slot's columns past its chunk's rows are zero
+        // in H^T, and the last slot is contracted up to its tile rows
+        const int64_t kbytes = (gslot * P.R_p + Rt) * P.eb;
+        EpiAccum epi{A.grad_W, d, (int)V, (int)d, (c == gslot && !A.accumulate_W) ? 1 : 0};
+        if (P.dw_bn == TileHead::BN) {
+          GemmShape g = make_shape<TileHead>(Gt, P.R_g, (int)V, Ht, P.R_g, (int)d, kbytes, 1, 4);
+          if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+        } else {
+          GemmShape g = make_shape<TileHeadNarrow>(Gt, P.R_g, (int)V, Ht, P.R_g, (int)d, kbytes, 1, 4);
+          if (launch_gemm<TileHeadNarrow, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+        }
       }
       mark(slot + 7, 1);
     }
@@ -578,6 +600,12 @@ size_t kd_topk_kl_fwd_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K
 
 size_t kd_topk_kl_bwd_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
   return kd::workspace_for(kd::kBackward, T, d, V, K, chunk, in_dtype);
+}
+
+int32_t kd_topk_kl_dw_chunks(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
+  kd::Plan p;
+  if (kd::make_plan(T, d, V, K, chunk, in_dtype, kd::kFused, &p) != KD_OK) return 0;
+  return p.dw_group;
 }
 
 static int32_t fwd_bwd_impl(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,

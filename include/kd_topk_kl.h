@@ -72,12 +72,26 @@ extern "C" {
 /*
  * Bytes of device workspace kd_topk_kl_fwd_bwd needs for these sizes; 0 if
  * the arguments are invalid.  A chunk larger than T is treated as T.  The
- * size grows as O(chunk*V + V*d) and does not depend on T beyond the chunk
- * (it holds one chunk's gradient in two layouts, the transposed head and
- * per-chunk row statistics).
+ * size grows as O(chunk*V + V*d) and does not depend on T beyond the chunk:
+ * it holds one chunk's gradient row-major, the transposed gradient of the
+ * chunks one head-gradient GEMM contracts (kd_topk_kl_dw_chunks), the
+ * transposed head and per-chunk row statistics.
  */
 size_t kd_topk_kl_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K,
                                   int64_t chunk, int32_t in_dtype);
+
+/*
+ * Number of consecutive chunks whose gradient one launch of the
+ * head-gradient GEMM (grad_W += G^T H) contracts, for these sizes; 0 if the
+ * arguments are invalid.  Each launch reads and writes the whole fp32
+ * grad_W once, so a launch takes consecutive chunks until it spans at least
+ * 4096 rows (the chunk counted rounded up to a multiple of 256), and never
+ * more chunks than there are: max(1, min(nchunks, 4096 / chunk_256)).  The
+ * same grouping applies to kd_topk_kl_bwd.  It changes neither the results'
+ * meaning nor the summation's determinism (fp32 sums in a fixed order).
+ */
+int32_t kd_topk_kl_dw_chunks(int64_t T, int64_t d, int64_t V, int64_t K,
+                             int64_t chunk, int32_t in_dtype);
 
 /*
  * Forward and backward of the loss above in one call.
@@ -133,7 +147,8 @@ int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype,
  *       teacher ids, 2 logsumexp merge, KL rows and the chunk's loss sum,
  *       3 recompute GEMM with the gradient epilogue, 4 sparse teacher
  *       scatter, 5 hidden-gradient GEMM, 6 its split-K reduction,
- *       7 head-gradient GEMM;
+ *       7 head-gradient GEMM (launched in the last chunk of each group of
+ *       kd_topk_kl_dw_chunks(...) chunks; empty in the group's others);
  *   i = KD_NUM_PHASES * nchunks      the prologue (count N, W^T);
  *   i = KD_NUM_PHASES * nchunks + 1  the final loss.
  * Everything else is as for kd_topk_kl_fwd_bwd; KD_ERR_NULL_ARG if events is

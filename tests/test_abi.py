@@ -22,7 +22,7 @@ def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {"kd_topk_kl_workspace_bytes", "kd_topk_kl_fwd_bwd",
                                           "kd_topk_kl_fwd_bwd_timed", "kd_status_str",
                                           "kd_topk_kl_fwd_workspace_bytes", "kd_topk_kl_bwd_workspace_bytes",
-                                          "kd_topk_kl_fwd", "kd_topk_kl_bwd",
+                                          "kd_topk_kl_dw_chunks", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
                                           "kd_topk_cache_workspace_bytes", "kd_topk_cache_build"}
 
 
@@ -52,12 +52,30 @@ def test_workspace_bytes_validation_and_scaling():
     assert a == b > 0
     # chunk larger than T is T
     assert wb(100, 64, 1000, 10, 5000, 0) == wb(100, 64, 1000, 10, 100, 0)
-    # O(chunk*V + V*d): doubling the chunk grows it by about 2 * 2 * chunk * V * 2 bytes
-    c1 = wb(65536, 2880, 201088, 100, 2048, 0)
-    c2 = wb(65536, 2880, 201088, 100, 4096, 0)
-    assert 0.9 < (c2 - c1) / (2 * 2048 * 201216 * 2) < 1.3
+    # O(chunk*V + V*d): past 4096 rows (one chunk per head-gradient launch)
+    # doubling the chunk grows both gradient layouts, 2 * chunk * V * 2 bytes
+    c1 = wb(65536, 2880, 201088, 100, 4096, 0)
+    c2 = wb(65536, 2880, 201088, 100, 8192, 0)
+    assert 0.9 < (c2 - c1) / (2 * 4096 * 201216 * 2) < 1.3
+    # below it the transposed layout spans 4096 rows of grouped chunks, so
+    # halving the chunk shrinks only the row-major one
+    c0 = wb(65536, 2880, 201088, 100, 2048, 0)
+    assert 0.9 < (c1 - c0) / (2048 * 201216 * 2) < 1.3
     # fp32 path is larger
     assert wb(512, 256, 4096, 16, 128, 1) > wb(512, 256, 4096, 16, 128, 0)
+
+
+def test_dw_chunks_grouping():
+    dc = kd.dw_chunks
+    assert dc(32768, 2880, 201088, 100, 2048, 0) == 2
+    assert dc(32768, 2880, 201088, 100, 4096, 0) == 1
+    assert dc(32768, 2880, 201088, 100, 8192, 0) == 1
+    assert dc(32768, 64, 1000, 10, 1000, 1) == 4        # 1000 rows count as 1024
+    assert dc(32768, 64, 1000, 10, 100, 0) == 16        # 100 rows count as 256
+    assert dc(3000, 64, 1000, 10, 1024, 0) == 3         # never more chunks than there are
+    assert dc(100, 64, 1000, 10, 5000, 0) == 1
+    assert dc(0, 64, 1000, 10, 100, 0) == 0             # invalid sizes
+    assert dc(100, 64, 1000, 10, 0, 0) == 0
 
 
 def _call(**kw):

@@ -79,6 +79,17 @@ def _small(T, d, V, K, dtype, seed, tau=1.0, masked=(), dup_row=None, mask_none=
                 tau=tau, chunk=4, dtype=dtype)
 
 
+def test_head_gradient_groups_of_chunks():
+    """1024-row chunks: one head-gradient launch contracts 4 chunks, so 6
+    chunks (the last ragged) make a full group and a partial one."""
+    import chunked_top_kl_lm_amd as kd
+    x = make_inputs(config_for(3, T=5220, d=128, V=3000), seed=5)
+    assert kd.dw_chunks(5220, 128, 3000, x["teacher_idx"].shape[1], 1024, kd.KD_BF16) == 4
+    g, ref = _check(x, "head-gradient groups", chunk=1024)
+    one = run_gpu(x, chunk=5220)                  # a single chunk and launch
+    assert rel_f(g["grad_W"], one["grad_W"]) < 1e-5
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [
     (6, 5, 11, 3, 1.0),       # d not a multiple of 64 (padded copies), V < one tile
