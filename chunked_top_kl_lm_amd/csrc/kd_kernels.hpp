@@ -248,7 +248,9 @@ struct EpiGrad {
   // 16 KB of the (now free) LDS ring twice, once per layout, so that both
   // layouts leave as 16-byte stores of whole 128/256-byte row segments
   // instead of 8-byte and 2-byte scattered stores (0.05-0.07 ms less per
-  // launch on the 32K workload's recompute GEMM).
+  // launch on the 32K workload's recompute GEMM).  The stores are
+  // non-temporal: the 1.6 GB a launch writes is read back only by later
+  // GEMMs, far beyond what the caches hold (another ~0.05 ms per launch).
   //   G staging  [64 t][128 v], 256-byte rows, 16-byte slot u of row t at
   //              u ^ (t & 15) (the 8-byte writes of a half-wave, 32 rows
   //              apart by 256 bytes, spread over the banks);
@@ -280,7 +282,7 @@ struct EpiGrad {
     for (int q = 0; q < 16; ++q) {
       const int t = 4 * q + (c.lane >> 4), u = c.lane & 15;
       const u32x4 val = *(const u32x4*)(lds + t * 256 + ((u ^ (t & 15)) << 4));
-      *(u32x4*)(G + (int64_t)(c.n0 + t) * ldg + c.m0 + 8 * u) = val;
+      __builtin_nontemporal_store(val, (u32x4*)(G + (int64_t)(c.n0 + t) * ldg + c.m0 + 8 * u));
     }
     // G^T staging (the wave's LDS operations run in order: the reads above
     // see the old contents)
@@ -307,7 +309,7 @@ struct EpiGrad {
     for (int q = 0; q < 16; ++q) {
       const int v = 8 * q + (c.lane >> 3), u = c.lane & 7;
       const u32x4 val = *(const u32x4*)(lds + v * 128 + ((u * 16) ^ (((v >> 2) & 1) << 6)));
-      *(u32x4*)(Gt + (int64_t)(c.m0 + v) * ldgt + c.n0 + 8 * u) = val;
+      __builtin_nontemporal_store(val, (u32x4*)(Gt + (int64_t)(c.m0 + v) * ldgt + c.n0 + 8 * u));
     }
   }
 
@@ -346,7 +348,8 @@ struct EpiStoreSplit {
 };
 
 // Head gradient: grad_W[v][j] (+)= tile, accumulated across chunks in fp32
-// (the first chunk stores).
+// (the first chunk stores).  grad_W (2.3 GB at V = 201088, d = 2880) is
+// streamed once per launch, so its loads and stores are non-temporal.
 struct EpiAccum {
   float* out;
   int64_t ld;
@@ -365,7 +368,8 @@ struct EpiAccum {
           for (int j = 0; j < FN; ++j) {
             const float* p = out + (int64_t)(c.m0 + 32 * i) * ld + c.n0 + 32 * j + acc_col(c.lane);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] += p[(int64_t)acc_row(r, c.lane) * ld];
+            for (int r = 0; r < 16; ++r)
+              acc[i][j][r] += __builtin_nontemporal_load(p + (int64_t)acc_row(r, c.lane) * ld);
           }
       }
 #pragma unroll
@@ -374,7 +378,8 @@ struct EpiAccum {
         for (int j = 0; j < FN; ++j) {
           float* p = out + (int64_t)(c.m0 + 32 * i) * ld + c.n0 + 32 * j + acc_col(c.lane);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) p[(int64_t)acc_row(r, c.lane) * ld] = acc[i][j][r];
+          for (int r = 0; r < 16; ++r)
+            __builtin_nontemporal_store(acc[i][j][r], p + (int64_t)acc_row(r, c.lane) * ld);
         }
       return;
     }
@@ -390,7 +395,7 @@ struct EpiAccum {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int mc = min(c.m0 + 32 * i + acc_row(r, c.lane), M - 1);
-            acc[i][j][r] += out[(int64_t)mc * ld + nc];
+            acc[i][j][r] += __builtin_nontemporal_load(out + (int64_t)mc * ld + nc);
           }
         }
     }
@@ -403,7 +408,7 @@ struct EpiAccum {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = c.m0 + 32 * i + acc_row(r, c.lane);
-          if (m < M) out[(int64_t)m * ld + n] = acc[i][j][r];
+          if (m < M) __builtin_nontemporal_store(acc[i][j][r], out + (int64_t)m * ld + n);
         }
       }
   }
