@@ -27,6 +27,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace kd {
@@ -128,6 +129,23 @@ struct EpiCtx {
   int wid, nwaves;
   char* smem;       // the LDS ring (free once the main loop has ended)
   int smem_bytes;   // its size
+  uint32_t pf[12];  // values an epilogue loaded ahead (see prefetch below)
+};
+
+// Epilogue prefetch.  An epilogue that reads small per-tile inputs (hit
+// lists, row scales) may declare kPrefetchSteps = n > 0 and a method
+// prefetch<FM, FN>(EpiCtx&, int step): the kernel calls it with step 0 before the
+// first K stage and with steps 1..n after main-loop stages 0..n-1, so each
+// step's loads have returned before the next step (every stage ends with
+// a wait for all of the wave's loads), and the latency of dependent loads
+// hides behind the MFMAs instead of stalling the epilogue.
+template <class T, class = void>
+struct PrefetchSteps {
+  static constexpr int value = 0;
+};
+template <class T>
+struct PrefetchSteps<T, std::void_t<decltype(T::kPrefetchSteps)>> {
+  static constexpr int value = T::kPrefetchSteps;
 };
 
 // ---------------------------------------------------------------------------
@@ -305,6 +323,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
   const int wid = tid >> 6;
   const int wm = wid / WN, wn = wid - (wid / WN) * WN;
 
+  constexpr int PS = PrefetchSteps<Epi>::value;
+  static_assert(PS == 0 || STAGES == 2, "prefetch steps rely on each stage waiting for all loads");
+  EpiCtx ctx;
+  ctx.m0 = pos.tm * BM + wm * C::TM;
+  ctx.n0 = pos.tn * BN + wn * C::TN;
+  ctx.lane = lane;
+  ctx.split = pos.split;
+  ctx.tm = pos.tm;
+  ctx.tn = pos.tn;
+  ctx.wm = wm;
+  ctx.wn = wn;
+  ctx.wid = wid;
+  ctx.nwaves = C::NW;
+  ctx.smem = smem;
+  ctx.smem_bytes = C::kLds;
+  if constexpr (PS > 0) epi.template prefetch<C::FM, C::FN>(ctx, 0);
+
   // g.k_tiles counts RB-byte K stages
   const int kt0 = pos.split * g.k_tiles_per_split;
   int kt1 = kt0 + g.k_tiles_per_split;
@@ -368,27 +403,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
     lds_barrier();
     read_frags<C>(smem, aRow0, bRow0, uoff[0], fa[0], fb[0]);
 
-    for (int it = 0; it < nk - 1; ++it)
+    for (int it = 0; it < nk - 1; ++it) {
       gemm_stage<E, C, BM, STAGES, true>(acc, fa, fb, smem, it, aRow0, bRow0, uoff, ra, rb, voffA, voffB, wid,
                                          kofs(it + STAGES));
+      if constexpr (PS > 0)
+        if (it < PS) epi.template prefetch<C::FM, C::FN>(ctx, it + 1);
+    }
     gemm_stage<E, C, BM, STAGES, false>(acc, fa, fb, smem, nk - 1, aRow0, bRow0, uoff, ra, rb, voffA, voffB, wid, 0u);
     wait_vmcnt<0>();                                       // drain the tail loads before LDS is reused
   }
+  if constexpr (PS > 0) {
+    // steps a short K loop did not reach, each after the previous one's loads
+    for (int s = (nk > 1 ? min(nk - 1, PS) : 0) + 1; s <= PS; ++s) {
+      __builtin_amdgcn_s_waitcnt(0);
+      epi.template prefetch<C::FM, C::FN>(ctx, s);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   lds_barrier();
 
-  EpiCtx ctx;
-  ctx.m0 = pos.tm * BM + wm * C::TM;
-  ctx.n0 = pos.tn * BN + wn * C::TN;
-  ctx.lane = lane;
-  ctx.split = pos.split;
-  ctx.tm = pos.tm;
-  ctx.tn = pos.tn;
-  ctx.wm = wm;
-  ctx.wn = wn;
-  ctx.wid = wid;
-  ctx.nwaves = C::NW;
-  ctx.smem = smem;
-  ctx.smem_bytes = C::kLds;
   epi.template apply<C::FM, C::FN>(acc, ctx);
 }
 

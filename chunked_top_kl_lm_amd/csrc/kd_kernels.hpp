@@ -46,7 +46,7 @@ __device__ __forceinline__ void clamp_padding_rows(f32x16 (&acc)[FM][FN], int ro
 // chunked KL loss", paragraph on Multiverse's two-part fix).
 //
 // The same epilogue also picks out the logits at the teacher's cached ids:
-// every (t, k) of the chunk is filed beforehand (build_hits) under the wave
+// every (t, k) of the chunk is filed beforehand (hit_build_kernel) under the wave
 // sub-tile that holds z[t, idx[t,k]], and the wave copies those values from
 // its accumulators to zsel[t*K + k].  The top-K gather of the KL thus reads
 // no W rows.
@@ -63,17 +63,37 @@ struct EpiLsePartial {
   float* zsel;          // [R * K] z at the teacher ids
   int hstride;          // offsets per row group: strips + 1
 
+  // The wave tile's hit-list bounds (step 0) and its first 64 entries
+  // (step 1) are loaded during the main loop.
+  static constexpr int kPrefetchSteps = 1;
+  template <int FM, int FN>
+  __device__ __forceinline__ void prefetch(EpiCtx& c, int step) const {
+    // raw values only: computing on a value right after its load would
+    // wait for it there
+    if (step == 0) {
+      const int b = (c.n0 / kHitT) * hstride + c.m0 / kHitV;
+      c.pf[0] = (uint32_t)hit_off[b];
+      c.pf[1] = (uint32_t)hit_off[b + 1];
+    } else {
+      const int e0 = (int)c.pf[0];
+      c.pf[1] -= c.pf[0];
+      const uint2 hv = c.lane < (int)c.pf[1] ? hits[e0 + c.lane] : make_uint2(0u, 0u);
+      c.pf[2] = hv.x;
+      c.pf[3] = hv.y;
+    }
+  }
+
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
     static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
     const int vt = c.m0 / (FM * 32);
     {
-      // the wave's entries, up to 64 per vector load, then one at a time
-      // from registers (no load latency per entry)
-      const int b = (c.n0 / kHitT) * hstride + vt;
-      const int e0 = hit_off[b], n = hit_off[b + 1] - e0;
+      // the wave's entries, up to 64 per vector load (the first 64 loaded
+      // ahead), then one at a time from registers
+      const int e0 = (int)c.pf[0], n = (int)c.pf[1];
       for (int base = 0; base < n; base += 64) {
-        const uint2 hv = base + c.lane < n ? hits[e0 + base + c.lane] : make_uint2(0u, 0u);
+        const uint2 hv = base == 0 ? make_uint2(c.pf[2], c.pf[3])
+                                   : (base + c.lane < n ? hits[e0 + base + c.lane] : make_uint2(0u, 0u));
         const int cnt = min(64, n - base);
         for (int q = 0; q < cnt; ++q) {
           const uint32_t hx = (uint32_t)__builtin_amdgcn_readlane((int)hv.x, q);
@@ -99,7 +119,7 @@ struct EpiLsePartial {
         if (c.lane < 32) part[(int64_t)vt * ldp + c.n0 + 32 * j + c.lane] = make_float2(-INFINITY, 0.f);
       return;
     }
-    clamp_padding_rows<FM, FN>(acc, rows_valid, c.lane);
+    if (rows_valid < FM * 32) clamp_padding_rows<FM, FN>(acc, rows_valid, c.lane);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       float mx = -INFINITY;
@@ -126,6 +146,9 @@ struct EpiLsePartial {
 // part -g (tau/N) m_t P[t,v] is subtracted in the epilogue from the fp32
 // values (fused call, through the forward's hit lists) or afterwards by
 // scatter_sparse_kernel (backward-only call).
+// Mask byte read for every row when the caller passes no mask.
+__device__ const uint8_t kMaskAll = 1;
+
 __device__ __forceinline__ float grad_scale(const int* count, const float* grad_loss, float tau) {
   const int N = *count;
   return N > 0 ? (grad_loss ? *grad_loss : 1.f) * (tau / (float)N) : 0.f;
@@ -152,15 +175,57 @@ struct EpiGrad {
   const float* psel;
   int hstride;
 
+  // Loaded during the main loop (EpiCtx::pf): step 0 the count N, g, the
+  // lane's columns' normalisers and mask bytes, and the hit-list bounds;
+  // step 1 the first 64 hit entries; step 2 their teacher probabilities.
+  //   pf: 0 e0, 1 end (n from step 1), 2-3 entry, 4 N, 5 g, 6+j lse,
+  //       8+j mask byte, 10 p
+  static constexpr int kPrefetchSteps = 2;
+  template <int FM, int FN>
+  __device__ __forceinline__ void prefetch(EpiCtx& c, int step) const {
+    static_assert(FN <= 2, "two prefetched columns per lane");
+    if (step == 0) {
+      c.pf[4] = (uint32_t)*count;
+      c.pf[5] = __builtin_bit_cast(uint32_t, grad_loss ? *grad_loss : 1.f);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        // raw loaded values only, from clamped addresses (rows past the
+        // chunk are zeroed in apply): a value that is computed on, or
+        // merged from two branches, right after its load is waited for there
+        const int nc = min(c.n0 + 32 * j + acc_col(c.lane), R - 1);
+        c.pf[6 + j] = __builtin_bit_cast(uint32_t, lse[nc]);
+        typedef const __attribute__((address_space(1))) uint8_t* GlobalByte;   // a global, not a flat, load
+        c.pf[8 + j] = (uint32_t)*(mask ? (GlobalByte)(mask + nc) : (GlobalByte)&kMaskAll);
+      }
+      c.pf[0] = c.pf[1] = 0u;
+      if (hit_off) {
+        const int b = (c.n0 / kHitT) * hstride + c.m0 / kHitV;
+        c.pf[0] = (uint32_t)hit_off[b];
+        c.pf[1] = (uint32_t)hit_off[b + 1];
+      }
+    } else if (step == 1) {
+      const int e0 = (int)c.pf[0];
+      c.pf[1] -= c.pf[0];
+      const uint2 hv = c.lane < (int)c.pf[1] ? hits[e0 + c.lane] : make_uint2(0u, 0u);
+      c.pf[2] = hv.x;
+      c.pf[3] = hv.y;
+    } else {
+      c.pf[10] = c.lane < (int)c.pf[1] ? __builtin_bit_cast(uint32_t, psel[c.pf[2]]) : 0u;
+    }
+  }
+
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
     // G values in fp32, in place: acc <- sc * q (sc = g tau m_t / N)
-    const float s = grad_scale(count, grad_loss, tau);
+    const int N = (int)c.pf[4];
+    const float s = N > 0 ? __builtin_bit_cast(float, c.pf[5]) * (tau / (float)N) : 0.f;
     float sc[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      float l2;
-      column(c.n0 + 32 * j + acc_col(c.lane), s, sc[j], l2);
+      // row scale (0 on masked rows and rows past the chunk) and base-2 normaliser
+      const bool row = c.n0 + 32 * j + acc_col(c.lane) < R;
+      sc[j] = row && c.pf[8 + j] ? s : 0.f;
+      const float l2 = row ? __builtin_bit_cast(float, c.pf[6 + j]) * lse_to2 : 0.f;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -176,29 +241,26 @@ struct EpiGrad {
     store_direct<FM, FN>(acc, c);
   }
 
-  // Row scale and base-2 normaliser of the lane's column n.
-  __device__ __forceinline__ void column(int n, float s, float& sc, float& l2) const {
-    sc = 0.f;
-    l2 = 0.f;
-    if (n < R) {
-      if (!mask || mask[n]) sc = s;
-      l2 = lse[n] * lse_to2;
-    }
-  }
-
   // -sc_t p_k at (v = idx[t,k], t) for every (t, k) filed under this wave
   // tile (duplicate ids each subtract their own p, so P sums them); the
   // lane that holds the element applies it, so G is rounded once.
   template <int FM, int FN>
   __device__ __forceinline__ void sparse_part(f32x16 (&acc)[FM][FN], const float (&sc)[FN], const EpiCtx& c) const {
     static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
-    const int b = (c.n0 / kHitT) * hstride + c.m0 / kHitV;
-    const int e0 = hit_off[b], n = hit_off[b + 1] - e0;
+    const int e0 = (int)c.pf[0], n = (int)c.pf[1];
     for (int base = 0; base < n; base += 64) {
-      // up to 64 entries and their p per vector load, then one at a time
+      // up to 64 entries and their p per vector load (the first 64 loaded
+      // ahead), then one at a time
       const bool in = base + c.lane < n;
-      const uint2 hv = in ? hits[e0 + base + c.lane] : make_uint2(0u, 0u);
-      const float pv = in ? psel[hv.x] : 0.f;
+      uint2 hv;
+      float pv;
+      if (base == 0) {
+        hv = make_uint2(c.pf[2], c.pf[3]);
+        pv = __builtin_bit_cast(float, c.pf[10]);
+      } else {
+        hv = in ? hits[e0 + base + c.lane] : make_uint2(0u, 0u);
+        pv = in ? psel[hv.x] : 0.f;
+      }
       const int cnt = min(64, n - base);
       for (int q = 0; q < cnt; ++q) {
         const uint32_t hy = (uint32_t)__builtin_amdgcn_readlane((int)hv.y, q);
