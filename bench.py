@@ -66,10 +66,12 @@ def cpu_baseline(x: dict, target_s: float) -> dict:
                  x["mask"][:n], x["tau"], rows_per_block=64)
         return time.perf_counter() - t0
 
-    n0 = 64
-    t0 = run(n0)
-    n = int(min(max(n0, round(n0 * target_s / max(t0, 1e-3) / 64) * 64), x["hidden"].shape[0]))
-    t = run(n) if n != n0 else t0
+    # size the sample from two short runs (fixed cost + cost per row)
+    t64, t128 = run(64), run(128)
+    per_row = max((t128 - t64) / 64, 1e-6)
+    fixed = max(t64 - 64 * per_row, 0.0)
+    n = int(min(max(64, round((target_s - fixed) / per_row / 64) * 64), x["hidden"].shape[0]))
+    t = run(n)
     T, d = x["hidden"].shape
     V = x["W"].shape[0]
     return {"value": n / t, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
@@ -78,18 +80,23 @@ def cpu_baseline(x: dict, target_s: float) -> dict:
             "seconds": t, "rows": n}
 
 
-def load_traffic(kernel: str):
+def workload_key(num: int, T: int, chunk: int) -> str:
+    return f"workload {num} T={T} chunk={chunk}"
+
+
+def load_traffic(kernel: str, workload: str, path: str = None):
     """HBM bytes per launch of a GEMM phase's kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy
-    calibration), if it was taken on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    calibration), if it was taken on the current kernel sources and this
+    workload; else None."""
+    p = path or os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(p):
         return None, None
     try:
         rec = json.load(open(p))
     except Exception:
         return None, None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload:
         return None, None
     k = rec.get("kernels", {}).get(kernel)
     if not k:
@@ -98,7 +105,7 @@ def load_traffic(kernel: str):
                                                  "copy_scale": rec.get("copy_scale")}
 
 
-def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
+def ingest_pmc(fetch_csv: str, write_csv: str, out: str = None) -> int:
     """Turn two rocprofv3 --pmc runs of `bench.py --steps 1 --warmup 0
     --copy-probe` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into
     profiles/pmc_traffic.json: per GEMM phase, the mean bytes per launch, each
@@ -124,9 +131,12 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
         kernels[phase] = {"fetch_bytes": scale["fetch"] * sum(f) / len(f),
                           "write_bytes": scale["write"] * sum(w) / len(w), "dispatches": len(f),
                           "fetch_raw_bytes": sum(f) / len(f), "write_raw_bytes": sum(w) / len(w)}
-    rec = {"kernel_source_hash": kernel_source_hash(), "copy_scale": scale,
+    from datagen import config_for
+    cfg = config_for(3)       # the counter runs use bench.py's default workload
+    rec = {"kernel_source_hash": kernel_source_hash(), "workload": workload_key(3, cfg.T, cfg.chunk),
+           "copy_scale": scale,
            "copy_raw_bytes": {"fetch": copy_f, "write": copy_w}, "kernels": kernels}
-    with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as fh:
+    with open(out or os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print("| phase | dispatches | fetch GB/launch | write GB/launch | raw fetch GB | raw write GB |")
     print("|---|---|---|---|---|---|")
@@ -309,7 +319,7 @@ def main() -> int:
     # a step (average over launches; the last chunk may be ragged)
     alg_flops = 2.0 * d * V * T / launches
     achieved = alg_flops / (launch_ms * 1e-3) / 1e12
-    traffic, traffic_detail = load_traffic(dom)
+    traffic, traffic_detail = load_traffic(dom, workload_key(args.workload, T, chunk))
 
     if args.copy_probe:
         src = torch.empty(2**30 // 2, dtype=torch.float32, device=dev).fill_(1.0)

@@ -301,9 +301,8 @@ __device__ __forceinline__ void gemm_stage(f32x16 (&acc)[C::FM][C::FN], u32x4 (&
 
 // One block per output tile (grid = all tiles, rounded up to a multiple of
 // 8): the dispatcher hands a CU its next tile as soon as the previous one
-// ends.  With the 96 KB LDS ring of a 256 x 256 tile one block fits per CU;
-// with the 72 KB ring of a 256 x 128 tile two blocks share a CU, so one
-// block's epilogue overlaps the other's main loop.
+// ends.  The 2-stage rings of the tiles in use (112-144 KB of LDS) fit one
+// block per CU.
 //
 // Each stage holds RB bytes of K (GROUPS = RB/32 K-groups).  Fragments are
 // read one group ahead into a second register set; before the last group's
