@@ -134,11 +134,12 @@ struct EpiCtx {
 
 // Epilogue prefetch.  An epilogue that reads small per-tile inputs (hit
 // lists, row scales) may declare kPrefetchSteps = n > 0 and a method
-// prefetch<FM, FN>(EpiCtx&, int step): the kernel calls it with step 0 before the
-// first K stage and with steps 1..n after main-loop stages 0..n-1, so each
-// step's loads have returned before the next step (every stage ends with
-// a wait for all of the wave's loads), and the latency of dependent loads
-// hides behind the MFMAs instead of stalling the epilogue.
+// prefetch<FM, FN>(EpiCtx&, int step): the kernel calls it with step 0 before
+// the first K stage and with steps 1..n after main-loop stages 0, S-1, ...,
+// (n-1)(S-1) (S = STAGES), so each step's loads have returned before the next
+// step (the wait of a stage leaves only the DMA of the S-2 newer stages in
+// flight), and the latency of dependent loads hides behind the MFMAs instead
+// of stalling the epilogue.
 template <class T, class = void>
 struct PrefetchSteps {
   static constexpr int value = 0;
@@ -323,7 +324,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
   const int wm = wid / WN, wn = wid - (wid / WN) * WN;
 
   constexpr int PS = PrefetchSteps<Epi>::value;
-  static_assert(PS == 0 || STAGES == 2, "prefetch steps rely on each stage waiting for all loads");
+  // a prefetch issued after stage `it` has returned by the wait of stage
+  // it + STAGES - 1 (that wait leaves only the newer stages' DMA in flight)
+  constexpr int PGAP = STAGES - 1;
   EpiCtx ctx;
   ctx.m0 = pos.tm * BM + wm * C::TM;
   ctx.n0 = pos.tn * BN + wn * C::TN;
@@ -406,14 +409,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
       gemm_stage<E, C, BM, STAGES, true>(acc, fa, fb, smem, it, aRow0, bRow0, uoff, ra, rb, voffA, voffB, wid,
                                          kofs(it + STAGES));
       if constexpr (PS > 0)
-        if (it < PS) epi.template prefetch<C::FM, C::FN>(ctx, it + 1);
+        if (it % PGAP == 0 && it / PGAP < PS) epi.template prefetch<C::FM, C::FN>(ctx, it / PGAP + 1);
     }
     gemm_stage<E, C, BM, STAGES, false>(acc, fa, fb, smem, nk - 1, aRow0, bRow0, uoff, ra, rb, voffA, voffB, wid, 0u);
     wait_vmcnt<0>();                                       // drain the tail loads before LDS is reused
   }
   if constexpr (PS > 0) {
     // steps a short K loop did not reach, each after the previous one's loads
-    for (int s = (nk > 1 ? min(nk - 1, PS) : 0) + 1; s <= PS; ++s) {
+    for (int s = (nk > 1 ? min((nk - 2) / PGAP + 1, PS) : 0) + 1; s <= PS; ++s) {
       __builtin_amdgcn_s_waitcnt(0);
       epi.template prefetch<C::FM, C::FN>(ctx, s);
     }
