@@ -10,7 +10,9 @@ bf16 hidden/W (a gpt-oss-20b-sized output head at 32K context).
 
 Prints ONE JSON line.  Extra keys: roofline (dominant kernel, live HIP-event
 timing inside the timed region), cpu_baseline (the fp64 oracle on a bounded
-sample of the same workload, host cores), phases_ms, peak_gib.
+sample of the same workload, host cores), mfma_ceiling (an MFMA-only loop on
+random operands timed after the step: what the MFMA pipes deliver at the
+clock the chip sustains), phases_ms, peak_gib.
 """
 from __future__ import annotations
 
@@ -82,6 +84,24 @@ def cpu_baseline(x: dict, target_s: float) -> dict:
 
 def workload_key(num: int, T: int, chunk: int) -> str:
     return f"workload {num} T={T} chunk={chunk}"
+
+
+def mfma_ceiling(kd, torch, dev, reps: int = 3) -> float:
+    """TFLOP/s of the MFMA-only probe (kd_mfma_probe: random bf16 register
+    operands, no memory traffic, the GEMMs' wave shape) at the clock the chip
+    sustains under it, timed with events on the current stream."""
+    blocks, iters = 1024, 2000
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    kd.mfma_probe(out, blocks, iters)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        kd.mfma_probe(out, blocks, iters)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return blocks * 8 * 64 * iters * 32768.0 / (ms * 1e-3) / 1e12
 
 
 def load_traffic(kernel: str, workload: str, path: str = None):
@@ -327,6 +347,8 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    ceiling = mfma_ceiling(kd, torch, dev) if dt == kd.KD_BF16 else None
+
     res = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -351,6 +373,9 @@ def main() -> int:
                      "frac": achieved / peak, "launch_ms": launch_ms,
                      "alg_flops_per_launch": alg_flops,
                      "traffic": traffic, "traffic_detail": traffic_detail},
+        "mfma_ceiling": None if ceiling is None else {
+            "tflops": ceiling, "what": "MFMA-only loop, random bf16 register operands, no memory traffic",
+            "frac_dominant": achieved / ceiling, "frac_step": tflops / ceiling},
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "wall_s_timed": wall,
         "input_gen_s": t_gen,

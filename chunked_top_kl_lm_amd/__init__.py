@@ -12,7 +12,7 @@ import os
 
 __all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
            "fwd", "bwd", "fwd_workspace_bytes", "bwd_workspace_bytes", "dw_chunks", "KdTopKKLFunction",
-           "kd_topk_kl_loss", "topk_cache", "topk_cache_workspace_bytes",
+           "kd_topk_kl_loss", "topk_cache", "mfma_probe", "topk_cache_workspace_bytes",
            "status_str", "STATUS"]
 
 KD_BF16 = 0
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.kd_topk_cache_workspace_bytes.restype = ctypes.c_size_t
         L.kd_topk_cache_build.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
         L.kd_topk_cache_build.restype = i32
+        L.kd_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
+        L.kd_mfma_probe.restype = i32
         L.kd_status_str.argtypes = [i32]
         L.kd_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -170,6 +172,19 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     if row_stats:
         return loss, gH, gW, rl, rk
     return loss, gH, gW
+
+
+def mfma_probe(out, blocks: int, iters: int, zero_operands: bool = False) -> None:
+    """Enqueue the sustained-MFMA-ceiling probe (kd_mfma_probe) on the
+    current stream; `out` is a float32 device tensor of blocks * 512
+    elements.  64 * iters MFMAs of 32768 FLOPs per wave, 8 waves per block."""
+    import torch
+    if out.dtype != torch.float32 or out.numel() < blocks * 512 or not out.is_contiguous():
+        raise ValueError("out: contiguous float32 with blocks * 512 elements")
+    stream = torch.cuda.current_stream(out.device).cuda_stream
+    rc = lib().kd_mfma_probe(int(blocks), int(iters), 1 if zero_operands else 0, _ptr(out), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KdError(rc)
 
 
 def topk_cache_workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> int:

@@ -29,6 +29,7 @@
 #include "../../include/kd_topk_kl.h"
 #include "kd_cache.hpp"
 #include "kd_kernels.hpp"
+#include "kd_probe.hpp"
 
 namespace kd {
 namespace {
@@ -681,6 +682,14 @@ int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype,
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == KD_BF16) return kd::run_cache<kd::Bf16>(p, hidden, W, out_idx, out_logit, (char*)workspace, s);
   return kd::run_cache<kd::F32>(p, hidden, W, out_idx, out_logit, (char*)workspace, s);
+}
+
+int32_t kd_mfma_probe(int32_t blocks, int32_t iters, int32_t zero_operands, float* out, void* stream) {
+  if (!out) return KD_ERR_NULL_ARG;
+  if (blocks < 1 || iters < 1) return KD_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(kd::mfma_probe_kernel, dim3((unsigned)blocks), dim3(512), 0, (hipStream_t)stream, (int)iters,
+                     zero_operands ? 1 : 0, out);
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP;
 }
 
 const char* kd_status_str(int32_t s) {

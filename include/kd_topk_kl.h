@@ -257,6 +257,21 @@ int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype,
                             int32_t* out_idx, float* out_logit,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement only (not part of the loss): the sustained bf16 MFMA ceiling.
+ * Enqueues `blocks` blocks of 512 threads; every wave issues
+ * 64 * iters v_mfma_f32_32x32x16_bf16 (32768 FLOPs each) back to back on
+ * register operands, in the GEMMs' wave shape, with random bf16 operands
+ * (or zeros when zero_operands != 0).  Timing it with events gives the
+ * MFMA throughput at the clock the chip sustains under that load, the
+ * ceiling the GEMMs are compared against beside the datasheet peak.
+ *  out   device float32 [blocks * 512] (written: per-thread accumulator
+ *        sums, 0 exactly with zero operands).
+ * Returns KD_ERR_NULL_ARG, KD_ERR_BAD_SHAPE (blocks or iters < 1) or
+ * KD_ERR_HIP on a launch failure, else KD_OK.
+ */
+int32_t kd_mfma_probe(int32_t blocks, int32_t iters, int32_t zero_operands, float* out, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kd_status_str(int32_t status);
 

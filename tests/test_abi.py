@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
                                           "kd_topk_kl_fwd_bwd_timed", "kd_status_str",
                                           "kd_topk_kl_fwd_workspace_bytes", "kd_topk_kl_bwd_workspace_bytes",
                                           "kd_topk_kl_dw_chunks", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
-                                          "kd_topk_cache_workspace_bytes", "kd_topk_cache_build"}
+                                          "kd_topk_cache_workspace_bytes", "kd_topk_cache_build",
+                                          "kd_mfma_probe"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -186,3 +187,10 @@ def test_topk_cache_host_argument_errors(kw, code):
     v = lambda x: None if x is None else ctypes.c_void_p(x)
     assert kd.lib().kd_topk_cache_build(v(a["hidden"]), v(a["W"]), a["dt"], a["T"], a["d"], a["V"], a["K"],
                                         a["chunk"], v(a["idx"]), v(a["logit"]), v(a["ws"]), a["wsb"], None) == code
+
+
+def test_mfma_probe_host_errors():
+    L = kd.lib()
+    assert L.kd_mfma_probe(1, 1, 0, None, None) == 1                          # NULL out
+    assert L.kd_mfma_probe(0, 1, 0, ctypes.c_void_p(0x10000), None) == 2     # no blocks
+    assert L.kd_mfma_probe(1, 0, 0, ctypes.c_void_p(0x10000), None) == 2     # no iterations
