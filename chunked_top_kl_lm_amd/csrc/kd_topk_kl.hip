@@ -122,9 +122,9 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
     return KD_ERR_BAD_SHAPE;
   if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_g * P.eb >= (1ll << 32))
     return KD_ERR_BAD_SHAPE;
-  // hit-list entries are int32-indexed
-  // hit lists: int32 entry indices; a row group's strip counts sit in LDS
-  if (P.R_p * K >= (1ll << 31) || (P.nvt + 1) * 4 > 65536) return KD_ERR_BAD_SHAPE;
+  // hit lists (forward): int32 entry indices; a row group's strip counts
+  // sit in 64 KB of LDS, so V_p / 128 + 1 <= 16384, i.e. V <= 2096896
+  if (P.R_p * K >= (1ll << 31) || (P.fwd && (P.nvt + 1) * 4 > 65536)) return KD_ERR_BAD_SHAPE;
   // split-K of the hidden-gradient GEMM (output only chunk x d): pick the
   // split count whose grid fills whole waves of 256 CUs best, with at least
   // one full wave, and a small penalty per split for the partial-sum traffic.

@@ -53,7 +53,7 @@ extern "C" {
 #define KD_ERR_NULL_ARG 1    /* a required pointer is NULL                      */
 #define KD_ERR_BAD_SHAPE 2   /* T, d, V or K < 1, K > V, K > KD_MAX_K, V*d,     */
                              /* chunk*V or T*d beyond what the kernels address, */
-                             /* or (loss, forward) V > 2097024                  */
+                             /* or (loss, forward) V > 2096896                  */
 #define KD_ERR_BAD_TAU 3     /* tau <= 0 or not finite                          */
 #define KD_ERR_BAD_CHUNK 4   /* chunk < 1                                       */
 #define KD_ERR_DTYPE 5       /* in_dtype is not KD_BF16 or KD_F32               */

@@ -90,6 +90,30 @@ def test_head_gradient_groups_of_chunks():
     assert rel_f(g["grad_W"], one["grad_W"]) < 1e-5
 
 
+def test_maximum_vocabulary():
+    """The largest vocabulary the forward accepts: V = 2096896 (its hit-list
+    strip counts, V/128 + 1 ints, fill 64 KB of LDS), a few rows."""
+    x = _small(40, 64, 2096896, 100, "bf16", seed=11, masked=(3,), dup_row=5)
+    _check(x, "max V", chunk=32)
+
+
+def test_maximum_cache_width():
+    """K = KD_MAX_K = 4096 ids per row (with a duplicate), fused and split
+    backward (whose sparse scatter merges duplicates in LDS)."""
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    from tests.gpu_util import to_device
+    x = _small(24, 64, 6000, 4096, "bf16", seed=12, masked=(1,), dup_row=2)
+    g, ref = _check(x, "max K", chunk=16)
+    t = to_device(x)
+    args = (t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"])
+    _, rl = kd.fwd(*args, tau=x["tau"], chunk=16)
+    gH, gW, _ = kd.bwd(*args, rl, tau=x["tau"], chunk=16)
+    torch.cuda.synchronize()
+    assert rel_f(gH.cpu().numpy(), ref["grad_hidden"]) <= GRAD_TOL
+    assert rel_f(gW.cpu().numpy(), ref["grad_W"]) <= GRAD_TOL
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [
     (6, 5, 11, 3, 1.0),       # d not a multiple of 64 (padded copies), V < one tile

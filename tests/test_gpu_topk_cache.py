@@ -12,8 +12,9 @@ and verify the rest:
     K-th and (K+1)-th logits are further apart, the ids equal the oracle's.
 Cases: the 32-row-block threshold path, the collect-everything path (fewer
 blocks than K), fp32 inputs, padded d, ragged chunks, exact ties (duplicated
-head rows), fully tied rows (the exact fallback), K = V, the full-size head
-at reduced T, and the cache feeding the loss.
+head rows), fully tied rows (the exact fallback), K = V, K = 4096 (the
+maximum, both paths), the full-size head at reduced T, and the cache feeding
+the loss.
 """
 import numpy as np
 import pytest
@@ -124,6 +125,16 @@ def test_fully_tied_rows_take_the_fallback():
     H, W = _bf16(H), _bf16(W)
     idx, logit = _check(H, W, 24, 16, "bf16", "all logits tied", exact_ids=np.tile(np.arange(24), (20, 1)))
     assert np.all(logit == logit[:, :1])
+
+
+def test_maximum_cache_width():
+    """K = KD_MAX_K = 4096: with V = 6000 every logit is a candidate and fits
+    the 8192-entry list; with V = 10000 the list overflows and every row takes
+    the exact fallback (a sorted top-4096 in LDS)."""
+    rng = np.random.default_rng(8)
+    H = _bf16(rng.standard_normal((6, 64)))
+    _check(H, _bf16(rng.standard_normal((6000, 64)) * 0.3), 4096, 4, "bf16", "K = 4096, V = 6000")
+    _check(H, _bf16(rng.standard_normal((10000, 64)) * 0.3), 4096, 4, "bf16", "K = 4096, V = 10000")
 
 
 def test_full_size_head_reduced_rows():
