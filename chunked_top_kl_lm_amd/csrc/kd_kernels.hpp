@@ -420,6 +420,10 @@ struct EpiAccum {
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    if constexpr (FM == 2 && FN == 5) {
+      apply_wide(acc, c);
+      return;
+    }
     const bool full = c.m0 + FM * 32 <= M && c.n0 + FN * 32 <= N;
     if (full) {
       // old values first (one burst of loads), then the stores
@@ -473,6 +477,72 @@ struct EpiAccum {
           if (m < M) __builtin_nontemporal_store(acc[i][j][r], out + (int64_t)m * ld + n);
         }
       }
+  }
+
+  // 64 x 160 wave tiles (256 x 320 blocks, 18 KB of the freed LDS ring per
+  // wave).  Keeping all 160 old values of a lane in flight next to its 160
+  // accumulators would not fit the registers, so columns 96..159 of the
+  // wave's tile go through LDS and are updated with 16-byte accesses, while
+  // columns 0..95 are updated straight from the accumulators.  Requires N
+  // and ld multiples of 4 and a 16-byte aligned `out` (checked by the host).
+  // Rows >= M and columns >= N: loads from clamped addresses, no stores.
+  static constexpr int kWideStride = 72;   // floats per staged row: 288 B, so the
+                                           // two half-waves (rows 4 apart) hit
+                                           // disjoint banks
+  __device__ __forceinline__ void apply_wide(f32x16 (&acc)[2][5], const EpiCtx& c) const {
+    float* st = (float*)(c.smem + c.wid * (c.smem_bytes / c.nwaves));   // [64][72]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 3; j < 5; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st[(32 * i + acc_row(r, c.lane)) * kWideStride + 32 * (j - 3) + acc_col(c.lane)] = acc[i][j][r];
+    // columns 0..95 from the accumulators: all old values in flight, then the stores
+    if (!first) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int nc = min(c.n0 + 32 * j + acc_col(c.lane), N - 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int mc = min(c.m0 + 32 * i + acc_row(r, c.lane), M - 1);
+            acc[i][j][r] += __builtin_nontemporal_load(out + (int64_t)mc * ld + nc);
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int n = c.n0 + 32 * j + acc_col(c.lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = c.m0 + 32 * i + acc_row(r, c.lane);
+          if (m < M && n < N) __builtin_nontemporal_store(acc[i][j][r], out + (int64_t)m * ld + n);
+        }
+      }
+    // columns 96..159 from LDS: lane -> row 4q + lane/16, columns 4 (lane % 16) .. +3
+    __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the wave's staging writes are done
+    f32x4 v[16];
+    const int col = 4 * (c.lane & 15);
+    const int n = c.n0 + 96 + col;
+    const int nc = min(n, N - 4);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = 4 * q + (c.lane >> 4);
+      v[q] = *(const f32x4*)(st + row * kWideStride + col);
+      if (!first) {
+        const int mc = min(c.m0 + row, M - 1);
+        v[q] += __builtin_nontemporal_load((const f32x4*)(out + (int64_t)mc * ld + nc));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = c.m0 + 4 * q + (c.lane >> 4);
+      if (m < M && n < N) __builtin_nontemporal_store(v[q], (f32x4*)(out + (int64_t)m * ld + n));
+    }
   }
 };
 

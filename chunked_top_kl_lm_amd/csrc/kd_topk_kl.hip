@@ -19,7 +19,9 @@
 //                     the sparse teacher part P at the hit lists' entries
 //   (the backward-only entry point subtracts P with a scatter kernel instead)
 //     GEMM dH         split-K over the vocabulary, fixed-order reduction
-//     GEMM dW         grad_W (+)= G^T H_c in fp32
+//     GEMM dW         grad_W (+)= G^T H in fp32, once per group of
+//                     consecutive chunks spanning >= 4096 rows (their G^T
+//                     and H^T sit side by side in the workspace)
 //   finalize        loss = tau^2 * acc / N
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -42,9 +44,11 @@ namespace {
 //    64 x 160, 144 KB LDS) when that pads d less -- at d = 2880 the 320-wide
 //    tile covers d exactly where 256 wastes 6% of the columns;
 //  - the head-gradient GEMM (N = d, fp32 read-modify-write epilogue):
-//    256 x 192 (8 waves of 64 x 96, 112 KB LDS), or 256 x 128 when that pads
-//    d less.  Its epilogue keeps all grad_W loads of a wave in flight at once;
-//    with 256 x 256 tiles the registers allow only about an eighth of them.
+//    256 x 320 when that pads d no more than the alternatives (its epilogue
+//    updates 96 of a wave's 160 columns from the accumulators and the rest
+//    through LDS with 16-byte accesses; d a multiple of 4), else 256 x 192
+//    (8 waves of 64 x 96, 112 KB LDS) or 256 x 128, whichever pads d less.
+//    Those keep all grad_W loads of a wave in flight at once.
 template <int BM_, int BN_, int WM_, int WN_, int ST_, int RB_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_, RB = RB_;
@@ -81,6 +85,7 @@ struct Plan {
   bool pad_d;         // d is not a multiple of 64: use zero-padded copies
   int64_t d_p, V_p, R_p, Nd_p;
   int dh_bn, dw_bn;   // column tile (over d) of the hidden- and head-gradient GEMMs
+  bool dw_wide;       // head-gradient GEMM on 256 x 320 tiles (LDS-staged update)
   int dw_group;       // consecutive chunks whose G^T and H_c^T one head-gradient GEMM contracts
   int64_t R_g;        // dw_group * R_p: row stride of the G^T and H_c^T buffers
   int64_t nvt;        // LSE strips per row
@@ -111,6 +116,7 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.R_p = round_up(P.chunk, kBN);
   P.dh_bn = round_up(d, TileDhWide::BN) < round_up(d, TileMain::BN) ? TileDhWide::BN : TileMain::BN;
   P.dw_bn = round_up(d, TileHead::BN) <= round_up(d, TileHeadNarrow::BN) ? TileHead::BN : TileHeadNarrow::BN;
+  P.dw_wide = d % 4 == 0 && round_up(d, TileDhWide::BN) <= round_up(d, P.dw_bn);
   P.Nd_p = round_up(d, P.dh_bn);
   P.nvt = P.V_p / kWaveM;
   P.dw_group = P.bwd ? (int)std::max<int64_t>(1, std::min<int64_t>(P.nchunks, kDwRows / P.R_p)) : 1;
@@ -422,7 +428,10 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
         // in H^T, and the last slot is contracted up to its tile rows
         const int64_t kbytes = (gslot * P.R_p + Rt) * P.eb;
         EpiAccum epi{A.grad_W, d, (int)V, (int)d, (c == gslot && !A.accumulate_W) ? 1 : 0};
-        if (P.dw_bn == TileHead::BN) {
+        if (P.dw_wide && (((uintptr_t)A.grad_W) & 15) == 0) {
+          GemmShape g = make_shape<TileDhWide>(Gt, P.R_g, (int)V, Ht, P.R_g, (int)d, kbytes, 1, 4);
+          if (launch_gemm<TileDhWide, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
+        } else if (P.dw_bn == TileHead::BN) {
           GemmShape g = make_shape<TileHead>(Gt, P.R_g, (int)V, Ht, P.R_g, (int)d, kbytes, 1, 4);
           if (launch_gemm<TileHead, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
         } else {

@@ -123,6 +123,7 @@ def test_maximum_cache_width():
     (300, 192, 1000, 8, 1.3), # ragged vocabulary tile and chunk
     (70, 576, 3000, 12, 1.0), # 320-wide hidden-gradient tile, ragged in d
     (90, 704, 2500, 16, 0.8), # 192-wide head-gradient tile, ragged in d
+    (70, 1900, 3000, 12, 1.0),# 320-wide head-gradient tile (LDS-staged update), ragged in d
 ])
 def test_edge_shapes(dtype, shape):
     T, d, V, K, tau = shape
