@@ -233,7 +233,7 @@ def main() -> int:
     ap.add_argument("--T", type=int, default=None, help="override the sequence length")
     ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU-baseline time")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 2 GiB device copy (counter calibration)")
