@@ -99,8 +99,29 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_device(dev, **tensors):
+    """Every given tensor must live on the CUDA device `dev` (the library
+    dereferences the pointers on that GPU)."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise ValueError(f"{name} must be a CUDA tensor on {dev}")
+
+
+def _check_workspace(workspace, status):
+    import torch
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1):
+        raise ValueError("status must be an int32 tensor of at least one element")
+
+
 def _check_inputs(hidden, W, teacher_idx, teacher_logit, mask):
     import torch
+    if not hidden.is_cuda:
+        raise ValueError("hidden must be a CUDA tensor")
+    _check_device(hidden.device, W=W, teacher_idx=teacher_idx, teacher_logit=teacher_logit, mask=mask)
+    if hidden.dim() != 2 or W.dim() != 2 or teacher_idx.dim() != 2:
+        raise ValueError("shapes: hidden [T,d], W [V,d], teacher_idx and teacher_logit [T,K]")
     T, d = hidden.shape
     V = W.shape[0]
     K = teacher_idx.shape[1]
@@ -152,6 +173,13 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     else:
         loss, gH, gW = out[:3]
         rl, rk = (out[3], out[4]) if row_stats else (None, None)
+        for name, t, shape in (("loss", loss, ()), ("grad_hidden", gH, (T, d)), ("grad_W", gW, (V, d)),
+                               ("row_lse", rl, (T,)), ("row_kl", rk, (T,))):
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()):
+                raise ValueError(f"out: {name} must be a contiguous float32 tensor of shape {shape}")
+        _check_device(dev, loss=loss, grad_hidden=gH, grad_W=gW, row_lse=rl, row_kl=rk)
+    _check_device(dev, workspace=workspace, status=status)
+    _check_workspace(workspace, status)
     nbytes = workspace_bytes(T, d, V, K, chunk, dt)
     if nbytes == 0:
         raise KdError(2)
@@ -179,8 +207,8 @@ def mfma_probe(out, blocks: int, iters: int, zero_operands: bool = False) -> Non
     current stream; `out` is a float32 device tensor of blocks * 512
     elements.  64 * iters MFMAs of 32768 FLOPs per wave, 8 waves per block."""
     import torch
-    if out.dtype != torch.float32 or out.numel() < blocks * 512 or not out.is_contiguous():
-        raise ValueError("out: contiguous float32 with blocks * 512 elements")
+    if out.dtype != torch.float32 or out.numel() < blocks * 512 or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out: contiguous float32 CUDA tensor with blocks * 512 elements")
     stream = torch.cuda.current_stream(out.device).cuda_stream
     rc = lib().kd_mfma_probe(int(blocks), int(iters), 1 if zero_operands else 0, _ptr(out), ctypes.c_void_p(stream))
     if rc != 0:
@@ -206,7 +234,11 @@ def topk_cache(hidden, W, K: int = 100, chunk: int = 2048, workspace=None):
         raise TypeError("hidden must be bfloat16 or float32")
     if W.dtype != hidden.dtype or W.shape[1] != d or not (hidden.is_contiguous() and W.is_contiguous()):
         raise ValueError("hidden [T,d] and W [V,d]: contiguous, same dtype")
+    if not hidden.is_cuda:
+        raise ValueError("hidden must be a CUDA tensor")
     dev = hidden.device
+    _check_device(dev, W=W, workspace=workspace)
+    _check_workspace(workspace, None)
     idx = torch.empty((T, K), dtype=torch.int32, device=dev)
     logit = torch.empty((T, K), dtype=torch.float32, device=dev)
     nbytes = topk_cache_workspace_bytes(T, d, V, K, chunk, dt)
@@ -230,6 +262,8 @@ def fwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chun
     import torch
     T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
     dev = hidden.device
+    _check_device(dev, workspace=workspace, status=status)
+    _check_workspace(workspace, status)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     rl = torch.empty(T, dtype=torch.float32, device=dev)
     rk = torch.empty(T, dtype=torch.float32, device=dev) if row_kl else None
@@ -261,6 +295,9 @@ def bwd(hidden, W, teacher_idx, teacher_logit, mask, row_lse, tau: float = 1.0, 
     import torch
     T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
     dev = hidden.device
+    _check_device(dev, row_lse=row_lse, grad_loss=grad_loss, accumulate_into=accumulate_into,
+                  workspace=workspace, status=status)
+    _check_workspace(workspace, status)
     if row_lse.dtype != torch.float32 or tuple(row_lse.shape) != (T,) or not row_lse.is_contiguous():
         raise ValueError("row_lse must be a contiguous float32 [T] tensor")
     if grad_loss is not None and (grad_loss.dtype != torch.float32 or grad_loss.numel() != 1):
