@@ -139,6 +139,15 @@ struct EpiLsePartial {
   }
 };
 
+// Gradient scale g tau / N (0 when no position counts).
+__device__ __forceinline__ float grad_scale(const int* count, const float* grad_loss, float tau) {
+  const int N = *count;
+  return N > 0 ? (grad_loss ? *grad_loss : 1.f) * (tau / (float)N) : 0.f;
+}
+
+// Mask byte read for every row when the caller passes no mask.
+__device__ const uint8_t kMaskAll = 1;
+
 // Backward recompute of a chunk: the logit gradient of the loss,
 // G[t,v] = g (tau/N) m_t q[t,v] (g = dL/dloss from the caller, 1 in the
 // fused call), written in two layouts (G [R_p][V_p] and G^T [V_p][R_p]) for
@@ -146,14 +155,6 @@ struct EpiLsePartial {
 // part -g (tau/N) m_t P[t,v] is subtracted in the epilogue from the fp32
 // values (fused call, through the forward's hit lists) or afterwards by
 // scatter_sparse_kernel (backward-only call).
-// Mask byte read for every row when the caller passes no mask.
-__device__ const uint8_t kMaskAll = 1;
-
-__device__ __forceinline__ float grad_scale(const int* count, const float* grad_loss, float tau) {
-  const int N = *count;
-  return N > 0 ? (grad_loss ? *grad_loss : 1.f) * (tau / (float)N) : 0.f;
-}
-
 template <class E>
 struct EpiGrad {
   typename E::T* G;
