@@ -190,18 +190,41 @@ def bench_topk_cache(args, cfg, chunk) -> int:
     K = cfg.K
     dt = kd.KD_BF16 if x["dtype"] == "bf16" else kd.KD_F32
     ws = torch.empty(kd.topk_cache_workspace_bytes(T, d, V, K, chunk, dt), dtype=torch.uint8, device=dev)
+    nchunks = -(-T // min(chunk, T))
+    nslots = kd.KD_CACHE_PHASES * nchunks + 1
     for _ in range(args.warmup):
         kd.topk_cache(H, W, K=K, chunk=chunk, workspace=ws)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    ev_sets = []
     for _ in range(args.steps):
-        kd.topk_cache(H, W, K=K, chunk=chunk, workspace=ws)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nslots)]
+        for e in evs:
+            e.record()
+        ev_sets.append(evs)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / args.steps
+    start.record()
+    for i in range(args.steps):
+        kd.topk_cache(H, W, K=K, chunk=chunk, workspace=ws, events=ev_sets[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    phase_ms = {p: 0.0 for p in kd.CACHE_PHASES}
+    for evs in ev_sets:
+        for c in range(nchunks):
+            for p, name in enumerate(kd.CACHE_PHASES):
+                k = c * kd.KD_CACHE_PHASES + p
+                phase_ms[name] += evs[2 * k].elapsed_time(evs[2 * k + 1]) / args.steps
     flops = 4.0 * T * d * V
     peak = PEAK_BF16_TFLOPS if dt == kd.KD_BF16 else PEAK_F32_TFLOPS
     tflops = flops / (ms * 1e-3) / 1e12
+    # dominant kernel: the heavier of the two head-GEMM passes, one launch per
+    # chunk, 2*d*V FLOPs per row
+    dom = max(("gemm_block_max", "gemm_collect"), key=lambda k: phase_ms[k])
+    launch_ms = phase_ms[dom] / nchunks
+    alg_flops = 2.0 * d * V * T / nchunks
+    achieved = alg_flops / (launch_ms * 1e-3) / 1e12
+    ceiling = mfma_ceiling(kd, torch, dev) if dt == kd.KD_BF16 else None
     res = {"metric": "tokens/sec top-K teacher-logit cache build (two head-GEMM passes, 4*T*d*V FLOPs)",
            "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -209,15 +232,30 @@ def bench_topk_cache(args, cfg, chunk) -> int:
            "config": {"workload": f"top-K cache of a {cfg.name} head: T={T} d={d} V={V} K={K} chunk={chunk}",
                       "T": T, "d": d, "V": V, "K": K, "chunk": chunk},
            "tflops": tflops, "pct_mfma_peak": 100.0 * tflops / peak,
-           "peak_gib": torch.cuda.max_memory_allocated() / 2**30}
+           "peak_gib": torch.cuda.max_memory_allocated() / 2**30,
+           "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                        "frac": achieved / peak, "launch_ms": launch_ms, "alg_flops_per_launch": alg_flops,
+                        "traffic": None, "traffic_detail": None},
+           "mfma_ceiling": None if ceiling is None else {
+               "tflops": ceiling, "what": "MFMA-only loop, random bf16 register operands, no memory traffic",
+               "frac_dominant": achieved / ceiling, "frac_step": tflops / ceiling},
+           "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()}}
     if not args.no_cpu_baseline:
         from oracle import topk_cache
-        n = 64
-        t0 = time.perf_counter()
-        topk_cache(x["hidden"][:n], x["W"], K)
-        sec = time.perf_counter() - t0
+
+        def run(n):
+            t0 = time.perf_counter()
+            topk_cache(x["hidden"][:n], x["W"], K)
+            return time.perf_counter() - t0
+
+        # size the sample from two short runs (fixed cost + cost per row)
+        t32, t64 = run(32), run(64)
+        per_row = max((t64 - t32) / 32, 1e-6)
+        n = int(min(max(32, round((args.cpu_seconds - max(t32 - 32 * per_row, 0.0)) / per_row / 32) * 32), T))
+        sec = run(n)
         res["cpu_baseline"] = {"value": n / sec, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
-                               "sample": f"first {n} of {T} rows, full d={d} V={V}, fp64 ({sec:.1f} s)"}
+                               "sample": f"first {n} of {T} rows, full d={d} V={V}, fp64 ({sec:.1f} s)",
+                               "seconds": sec, "rows": n}
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
@@ -237,6 +275,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 2 GiB device copy (counter calibration)")
+    ap.add_argument("--split", action="store_true",
+                    help="time the split entry points (forward call, then backward call) instead of the fused call")
     ap.add_argument("--topk-cache", action="store_true",
                     help="measure the offline top-K cache builder on the workload's head instead of the loss")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -275,7 +315,9 @@ def main() -> int:
     V = t["W"].shape[0]
     K = t["teacher_idx"].shape[1]
     dt = kd.KD_BF16 if x["dtype"] == "bf16" else kd.KD_F32
-    ws = torch.empty(kd.workspace_bytes(T, d, V, K, chunk, dt), dtype=torch.uint8, device=dev)
+    ws_bytes = (max(kd.fwd_workspace_bytes(T, d, V, K, chunk, dt), kd.bwd_workspace_bytes(T, d, V, K, chunk, dt))
+                if args.split else kd.workspace_bytes(T, d, V, K, chunk, dt))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     out = (torch.empty((), dtype=torch.float32, device=dev), torch.empty((T, d), dtype=torch.float32, device=dev),
            torch.empty((V, d), dtype=torch.float32, device=dev))
@@ -283,9 +325,17 @@ def main() -> int:
     nchunks = -(-T // eff_chunk)
     nslots = kd.KD_NUM_PHASES * nchunks + 2
 
+    ncalls = 2 if args.split else 1        # event sets per step
+
     def call(events=None):
-        kd.fwd_bwd(t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"], tau=x["tau"],
-                   chunk=chunk, workspace=ws, status=status, out=out, events=events)
+        if not args.split:
+            kd.fwd_bwd(t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"], tau=x["tau"],
+                       chunk=chunk, workspace=ws, status=status, out=out, events=events and events[0])
+            return
+        args5 = (t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"])
+        _, rl = kd.fwd(*args5, tau=x["tau"], chunk=chunk, workspace=ws, status=status,
+                       events=events and events[0])
+        kd.bwd(*args5, rl, tau=x["tau"], chunk=chunk, workspace=ws, status=status, events=events and events[1])
 
     for _ in range(args.warmup):
         call()
@@ -294,10 +344,13 @@ def main() -> int:
     # per-step event sets (created by recording once)
     ev_sets = []
     for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nslots)]
-        for e in evs:
-            e.record()
-        ev_sets.append(evs)
+        per_call = []
+        for _ in range(ncalls):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nslots)]
+            for e in evs:
+                e.record()
+            per_call.append(evs)
+        ev_sets.append(per_call)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -315,14 +368,15 @@ def main() -> int:
     # phase times per call
     phase_ms = {p: 0.0 for p in kd.PHASES}
     pro = fin = 0.0
-    for evs in ev_sets:
-        for c in range(nchunks):
-            for p, name in enumerate(kd.PHASES):
-                i = c * kd.KD_NUM_PHASES + p
-                phase_ms[name] += evs[2 * i].elapsed_time(evs[2 * i + 1])
-        i = kd.KD_NUM_PHASES * nchunks
-        pro += evs[2 * i].elapsed_time(evs[2 * i + 1])
-        fin += evs[2 * i + 2].elapsed_time(evs[2 * i + 3])
+    for per_call in ev_sets:
+        for evs in per_call:
+            for c in range(nchunks):
+                for p, name in enumerate(kd.PHASES):
+                    i = c * kd.KD_NUM_PHASES + p
+                    phase_ms[name] += evs[2 * i].elapsed_time(evs[2 * i + 1])
+            i = kd.KD_NUM_PHASES * nchunks
+            pro += evs[2 * i].elapsed_time(evs[2 * i + 1])
+            fin += evs[2 * i + 2].elapsed_time(evs[2 * i + 3])
     phase_ms = {k: v / args.steps for k, v in phase_ms.items()}
     phase_ms["prologue"] = pro / args.steps
     phase_ms["finalize"] = fin / args.steps
@@ -339,7 +393,7 @@ def main() -> int:
     # a step (average over launches; the last chunk may be ragged)
     alg_flops = 2.0 * d * V * T / launches
     achieved = alg_flops / (launch_ms * 1e-3) / 1e12
-    traffic, traffic_detail = load_traffic(dom, workload_key(args.workload, T, chunk))
+    traffic, traffic_detail = (None, None) if args.split else load_traffic(dom, workload_key(args.workload, T, chunk))
 
     if args.copy_probe:
         src = torch.empty(2**30 // 2, dtype=torch.float32, device=dev).fill_(1.0)
@@ -363,7 +417,8 @@ def main() -> int:
         "dtype": x["dtype"],
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: lm_head KL distillation T={T} d={d} V={V} K={K} "
-                               f"chunk={chunk} tau={x['tau']}",
+                               f"chunk={chunk} tau={x['tau']}"
+                               + (" (split forward and backward calls)" if args.split else ""),
                    "T": T, "d": d, "V": V, "K": K, "chunk": chunk, "tau": x["tau"],
                    "global_batch": 1, "seq_len": T, "parallelism": "single-gpu"},
         "tflops": tflops,

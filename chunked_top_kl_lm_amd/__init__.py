@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
+__all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KD_CACHE_PHASES", "CACHE_PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
            "fwd", "bwd", "fwd_workspace_bytes", "bwd_workspace_bytes", "dw_chunks", "KdTopKKLFunction",
            "kd_topk_kl_loss", "topk_cache", "mfma_probe", "topk_cache_workspace_bytes",
            "status_str", "STATUS"]
@@ -18,6 +18,8 @@ __all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KdError", "lib", "wo
 KD_BF16 = 0
 KD_F32 = 1
 KD_NUM_PHASES = 8
+KD_CACHE_PHASES = 4
+CACHE_PHASES = ("gemm_block_max", "threshold", "gemm_collect", "select")
 PHASES = ("chunk_prep", "gemm_fwd_lse", "kl_rows", "gemm_bwd_grad", "scatter_sparse",
           "gemm_dhidden", "dhidden_reduce", "gemm_dW")
 STATUS = {0: "KD_OK", 1: "KD_ERR_NULL_ARG", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_TAU",
@@ -66,6 +68,12 @@ def lib() -> ctypes.CDLL:
         L.kd_topk_cache_workspace_bytes.restype = ctypes.c_size_t
         L.kd_topk_cache_build.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
         L.kd_topk_cache_build.restype = i32
+        L.kd_topk_kl_fwd_timed.argtypes = L.kd_topk_kl_fwd.argtypes + [vp]
+        L.kd_topk_kl_fwd_timed.restype = i32
+        L.kd_topk_kl_bwd_timed.argtypes = L.kd_topk_kl_bwd.argtypes + [vp]
+        L.kd_topk_kl_bwd_timed.restype = i32
+        L.kd_topk_cache_build_timed.argtypes = L.kd_topk_cache_build.argtypes + [vp]
+        L.kd_topk_cache_build_timed.restype = i32
         L.kd_mfma_probe.argtypes = [i32, i32, i32, vp, vp]
         L.kd_mfma_probe.restype = i32
         L.kd_status_str.argtypes = [i32]
@@ -97,6 +105,11 @@ def dw_chunks(T: int, d: int, V: int, K: int, chunk: int, dtype: int) -> int:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _events(events):
+    """ctypes array of the hipEvent_t handles of already-recorded torch.cuda.Event objects."""
+    return (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
 
 
 def _check_device(dev, **tensors):
@@ -193,8 +206,7 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     if events is None:
         rc = L.kd_topk_kl_fwd_bwd(*args)
     else:
-        arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
-        rc = L.kd_topk_kl_fwd_bwd_timed(*args, arr)
+        rc = L.kd_topk_kl_fwd_bwd_timed(*args, _events(events))
     if rc != 0:
         raise KdError(rc)
     if row_stats:
@@ -219,10 +231,12 @@ def topk_cache_workspace_bytes(T: int, d: int, V: int, K: int, chunk: int, dtype
     return int(lib().kd_topk_cache_workspace_bytes(T, d, V, K, chunk, dtype))
 
 
-def topk_cache(hidden, W, K: int = 100, chunk: int = 2048, workspace=None):
+def topk_cache(hidden, W, K: int = 100, chunk: int = 2048, workspace=None, events=None):
     """Offline top-K cache of a teacher head (kd_topk_cache_build): returns
     (idx [T,K] int32, logit [T,K] float32), per row the K largest logits of
-    hidden @ W^T in descending order (equal logits: lower id first)."""
+    hidden @ W^T in descending order (equal logits: lower id first).
+    `events`, for measurement only: 2 * (KD_CACHE_PHASES * nchunks + 1)
+    already-recorded torch.cuda.Event objects (kd_topk_cache_build_timed)."""
     import torch
     T, d = hidden.shape
     V = W.shape[0]
@@ -247,18 +261,22 @@ def topk_cache(hidden, W, K: int = 100, chunk: int = 2048, workspace=None):
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib().kd_topk_cache_build(_ptr(hidden), _ptr(W), dt, T, d, V, K, int(chunk), _ptr(idx), _ptr(logit),
-                                   _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    args = (_ptr(hidden), _ptr(W), dt, T, d, V, K, int(chunk), _ptr(idx), _ptr(logit), _ptr(workspace),
+            workspace.numel(), ctypes.c_void_p(stream))
+    if events is None:
+        rc = lib().kd_topk_cache_build(*args)
+    else:
+        rc = lib().kd_topk_cache_build_timed(*args, _events(events))
     if rc != 0:
         raise KdError(rc)
     return idx, logit
 
 
 def fwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chunk: int = 2048,
-        row_kl: bool = False, workspace=None, status=None):
+        row_kl: bool = False, workspace=None, status=None, events=None):
     """Forward only (kd_topk_kl_fwd).  Returns (loss [0-d float32], row_lse
     [T] float32) and, with row_kl, also the per-row KL [T].  row_lse is what
-    bwd() needs."""
+    bwd() needs.  `events`: as for fwd_bwd (kd_topk_kl_fwd_timed)."""
     import torch
     T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
     dev = hidden.device
@@ -273,9 +291,13 @@ def fwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chun
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib().kd_topk_kl_fwd(_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit), _ptr(mask),
-                              T, d, V, K, float(tau), int(chunk), _ptr(loss), _ptr(rl), _ptr(rk),
-                              _ptr(workspace), workspace.numel(), _ptr(status), ctypes.c_void_p(stream))
+    args = (_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit), _ptr(mask), T, d, V, K,
+            float(tau), int(chunk), _ptr(loss), _ptr(rl), _ptr(rk), _ptr(workspace), workspace.numel(),
+            _ptr(status), ctypes.c_void_p(stream))
+    if events is None:
+        rc = lib().kd_topk_kl_fwd(*args)
+    else:
+        rc = lib().kd_topk_kl_fwd_timed(*args, _events(events))
     if rc != 0:
         raise KdError(rc)
     return (loss, rl, rk) if row_kl else (loss, rl)
@@ -283,7 +305,7 @@ def fwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chun
 
 def bwd(hidden, W, teacher_idx, teacher_logit, mask, row_lse, tau: float = 1.0, chunk: int = 2048,
         grad_loss=None, grad_hidden="float32", grad_W=True, accumulate_into=None, grad_W_bf16: bool = False,
-        workspace=None, status=None):
+        workspace=None, status=None, events=None):
     """Backward only (kd_topk_kl_bwd): gradients of grad_loss * loss.
 
     grad_loss: 0-d float32 CUDA tensor or None (= 1).  grad_hidden:
@@ -291,7 +313,8 @@ def bwd(hidden, W, teacher_idx, teacher_logit, mask, row_lse, tau: float = 1.0, 
     [V,d] tensor), False (not computed); accumulate_into: an fp32 [V,d] CUDA
     tensor that the head gradient is added to instead (returned as grad_W).
     grad_W_bf16: also return a bf16 copy of the final grad_W.  Returns
-    (grad_hidden, grad_W, grad_W_bf16), with None for what was not asked."""
+    (grad_hidden, grad_W, grad_W_bf16), with None for what was not asked.
+    `events`: as for fwd_bwd (kd_topk_kl_bwd_timed)."""
     import torch
     T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
     dev = hidden.device
@@ -321,10 +344,13 @@ def bwd(hidden, W, teacher_idx, teacher_logit, mask, row_lse, tau: float = 1.0, 
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib().kd_topk_kl_bwd(_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit), _ptr(mask),
-                              T, d, V, K, float(tau), int(chunk), _ptr(row_lse), _ptr(grad_loss), _ptr(gH),
-                              gh_code, _ptr(gW), acc, _ptr(gWb), _ptr(workspace), workspace.numel(), _ptr(status),
-                              ctypes.c_void_p(stream))
+    args = (_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit), _ptr(mask), T, d, V, K,
+            float(tau), int(chunk), _ptr(row_lse), _ptr(grad_loss), _ptr(gH), gh_code, _ptr(gW), acc, _ptr(gWb),
+            _ptr(workspace), workspace.numel(), _ptr(status), ctypes.c_void_p(stream))
+    if events is None:
+        rc = lib().kd_topk_kl_bwd(*args)
+    else:
+        rc = lib().kd_topk_kl_bwd_timed(*args, _events(events))
     if rc != 0:
         raise KdError(rc)
     return gH, gW, gWb

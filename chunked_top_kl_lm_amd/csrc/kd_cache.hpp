@@ -45,68 +45,91 @@ __device__ __forceinline__ uint64_t cand_key(float z, uint32_t id) {
 constexpr int kBlockRows = 32;   // vocabulary rows per block maximum
 
 // Pass 1: per 32-row vocabulary block and column (row t), the largest logit
-// of the block's valid rows.  out [ceil(V_p/32)][ldp].
+// of the block's valid rows, stored per row t: out[t][block].
 struct EpiBlockMax {
-  float* out;
-  int ldp;
+  float* out;   // [rows][ldb]: row t's block maxima contiguous
+  int ldb;      // V_p / 32 (a multiple of 8)
   int V;
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+    static_assert(FM == 4, "a wave strip holds four 32-row blocks (one 16-byte store per row)");
     const int rows_valid = V - c.m0;
     if (rows_valid <= 0) return;                    // no valid block here (never read)
-    clamp_padding_rows<FM, FN>(acc, rows_valid, c.lane);
+    if (rows_valid < FM * 32) clamp_padding_rows<FM, FN>(acc, rows_valid, c.lane);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+      float mx[FM];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        float mx = acc[i][j][0];
+      for (int i = 0; i < FM; ++i) {
+        float m = acc[i][j][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (c.lane < 32 && c.m0 + 32 * i < V) out[(int64_t)(c.m0 / kBlockRows + i) * ldp + c.n0 + 32 * j + c.lane] = mx;
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
+        mx[i] = fmaxf(m, __shfl_xor(m, 32));
       }
+      // lane < 32: column (row t) n0 + 32 j + lane, blocks m0/32 .. +3
+      if (c.lane < 32)
+        *(f32x4*)(out + (int64_t)(c.n0 + 32 * j + c.lane) * ldb + c.m0 / kBlockRows) =
+            f32x4{mx[0], mx[1], mx[2], mx[3]};
+    }
   }
 };
+
+// Inclusive prefix sum over the 256 threads of a block (4 waves).
+__device__ __forceinline__ int block_incl_scan_256(int v, int* s_w) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) s_w[w] = v;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += s_w[i];
+  __syncthreads();
+  return v + add;
+}
 
 // theta_t = the K-th largest of the row's nbv valid block maxima (MSB-first
 // radix select over 8-bit digits of the order-preserving keys), or -inf when
 // there are fewer than K blocks (then every logit is a candidate).  One
-// block of 256 threads per row.
-__global__ __launch_bounds__(256) void cache_threshold_kernel(const float* bmax, int ldp, int nbv, int K,
+// block of 256 threads per row; the row's maxima are read contiguously, each
+// wave counts into its own histogram, and the digit holding the rank is
+// found with a block-wide prefix sum over the bins in descending order.
+__global__ __launch_bounds__(256) void cache_threshold_kernel(const float* bmax, int ldb, int nbv, int K,
                                                               float* theta) {
-  __shared__ int hist[256];
+  __shared__ int hist[4][256];
+  __shared__ int s_w[4];
   __shared__ uint32_t s_prefix;
   __shared__ int s_k;
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   if (nbv < K) {
     if (tid == 0) theta[t] = -INFINITY;
     return;
   }
+  const float* row = bmax + (int64_t)t * ldb;
   uint32_t prefix = 0, mask = 0;
   int k = K;                                        // rank still to find among the matching keys
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
     __syncthreads();
     for (int i = tid; i < nbv; i += 256) {
-      const uint32_t key = fkey(bmax[(int64_t)i * ldp + t]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      const uint32_t key = fkey(row[i]);
+      if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0, dgt = 255;
-      for (; dgt > 0; --dgt) {
-        if (acc + hist[dgt] >= k) break;
-        acc += hist[dgt];
-      }
-      s_prefix = prefix | ((uint32_t)dgt << shift);
-      s_k = k - acc;
+    const int b = 255 - tid;                         // bins in descending order
+    const int cnt = hist[0][b] + hist[1][b] + hist[2][b] + hist[3][b];
+    const int incl = block_incl_scan_256(cnt, s_w);  // keys in bins >= b
+    if (incl >= k && incl - cnt < k) {               // exactly one bin holds rank k
+      s_prefix = prefix | ((uint32_t)b << shift);
+      s_k = k - (incl - cnt);
     }
     __syncthreads();
     prefix = s_prefix;
     k = s_k;
     mask |= 255u << shift;
-    __syncthreads();
   }
   if (tid == 0) theta[t] = fkey_inv(prefix);
 }

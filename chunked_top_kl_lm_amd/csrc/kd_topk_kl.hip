@@ -251,7 +251,13 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
   hipStream_t st = A.st;
   // timing markers (measurement entry point only)
   auto mark = [&](int64_t slot, int end) {
-    if (A.events) hipEventRecord((hipEvent_t)A.events[2 * slot + end], st);
+    if (A.events) (void)hipEventRecord((hipEvent_t)A.events[2 * slot + end], st);
+  };
+  // a phase this call does not run: both markers back to back (every event
+  // is recorded in every call, so each phase reads as a valid interval)
+  auto skip = [&](int64_t slot) {
+    mark(slot, 0);
+    mark(slot, 1);
   };
   const int64_t pro_slot = (int64_t)KD_NUM_PHASES * P.nchunks;
   int* count = (int*)(ws + P.off_scalar);
@@ -356,8 +362,14 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(256), 0, st, (const double*)rowkl, mask_c, R, loss_acc);
       KD_LAUNCH_CHECK();
       mark(slot + 2, 1);
+    } else {
+      skip(slot + 1);
+      skip(slot + 2);
     }
-    if (!P.bwd) continue;
+    if (!P.bwd) {
+      for (int p = 3; p < KD_NUM_PHASES; ++p) skip(slot + p);
+      continue;
+    }
 
     mark(slot + 3, 0);
     // backward recompute: G = (tau/N) m q, both layouts; the row normaliser
@@ -419,6 +431,9 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       }
       KD_LAUNCH_CHECK();
       mark(slot + 6, 1);
+    } else {
+      skip(slot + 5);
+      skip(slot + 6);
     }
     if (want_dw) {
       mark(slot + 7, 0);
@@ -440,6 +455,8 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
         }
       }
       mark(slot + 7, 1);
+    } else {
+      skip(slot + 7);
     }
   }
   mark(pro_slot + 1, 0);
@@ -526,7 +543,7 @@ int32_t make_cache_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chun
   size_t o = 0;
   P.off_wp = o; if (P.pad_d) o = align256(o + (size_t)V * P.d_p * e);
   P.off_hp = o; if (P.pad_d) o = align256(o + (size_t)P.R_p * P.d_p * e);
-  P.off_bmax = o; o = align256(o + (size_t)(P.V_p / kBlockRows) * P.R_p * sizeof(float));
+  P.off_bmax = o; o = align256(o + (size_t)P.R_p * (P.V_p / kBlockRows) * sizeof(float));   // [R_p][V_p/32]
   P.off_theta = o; o = align256(o + (size_t)P.R_p * sizeof(float));
   P.off_cnt = o; o = align256(o + (size_t)P.R_p * sizeof(int));
   P.off_cand = o; o = align256(o + (size_t)P.R_p * P.cap * sizeof(uint2));
@@ -537,8 +554,13 @@ int32_t make_cache_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chun
 
 template <class E>
 int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t* out_idx, float* out_logit, char* ws,
-                  hipStream_t st) {
+                  hipStream_t st, void* const* events) {
   typedef typename E::T T;
+  // timing markers (measurement entry point only): slot c * KD_CACHE_PHASES + p
+  // per chunk phase, slot KD_CACHE_PHASES * nchunks for the prologue
+  auto mark = [&](int64_t slot, int end) {
+    if (events) (void)hipEventRecord((hipEvent_t)events[2 * slot + end], st);
+  };
   T* Wp = (T*)(ws + P.off_wp);
   T* Hp = (T*)(ws + P.off_hp);
   float* bmax = (float*)(ws + P.off_bmax);
@@ -550,6 +572,7 @@ int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t
 
   const T* Wsrc = (const T*)W;
   int64_t ldw = d;
+  mark(KD_CACHE_PHASES * P.nchunks, 0);
   if (P.pad_d) {
     const int64_t n = V * P.d_p;
     hipLaunchKernelGGL(pad_kernel<E>, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
@@ -558,10 +581,13 @@ int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t
     Wsrc = Wp;
     ldw = P.d_p;
   }
+  mark(KD_CACHE_PHASES * P.nchunks, 1);
   const int64_t kbytes_d = P.d_p * P.eb;
   for (int64_t c = 0; c < P.nchunks; ++c) {
     const int64_t c0 = c * P.chunk;
     const int R = (int)std::min<int64_t>(P.chunk, P.T - c0);
+    const int64_t slot = c * KD_CACHE_PHASES;
+    mark(slot + 0, 0);
     const T* Hc = (const T*)hidden + c0 * d;
     const T* Hsrc = Hc;
     int64_t ldh = d;
@@ -577,12 +603,19 @@ int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t
     hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)cdiv(R, 256)), dim3(256), 0, st, cnt, (int64_t)R, 0);
     KD_LAUNCH_CHECK();
     GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-    if (launch_gemm<TileMain, E>(g, EpiBlockMax{bmax, (int)P.R_p, (int)V}, st) != hipSuccess) return KD_ERR_HIP;
-    hipLaunchKernelGGL(cache_threshold_kernel, dim3(R), dim3(256), 0, st, (const float*)bmax, (int)P.R_p,
-                       (int)P.nb32, (int)K, theta);
+    if (launch_gemm<TileMain, E>(g, EpiBlockMax{bmax, (int)(P.V_p / kBlockRows), (int)V}, st) != hipSuccess)
+      return KD_ERR_HIP;
+    mark(slot + 0, 1);
+    mark(slot + 1, 0);
+    hipLaunchKernelGGL(cache_threshold_kernel, dim3(R), dim3(256), 0, st, (const float*)bmax,
+                       (int)(P.V_p / kBlockRows), (int)P.nb32, (int)K, theta);
     KD_LAUNCH_CHECK();
+    mark(slot + 1, 1);
+    mark(slot + 2, 0);
     if (launch_gemm<TileMain, E>(g, EpiCollect{theta, cnt, cand, P.cap, (int)V, R}, st) != hipSuccess)
       return KD_ERR_HIP;
+    mark(slot + 2, 1);
+    mark(slot + 3, 0);
     int32_t* oi = out_idx + c0 * K;
     float* ol = out_logit + c0 * K;
     hipLaunchKernelGGL(cache_select_kernel, dim3(R), dim3(256), (size_t)P.cap * sizeof(uint64_t), st,
@@ -591,6 +624,7 @@ int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t
     hipLaunchKernelGGL(cache_fallback_kernel<E>, dim3(R), dim3(256), (size_t)2 * P.half * sizeof(uint64_t), st, Hc,
                        d, (const T*)W, d, (int)d, (int)V, (int)K, P.half, (const int*)ovf, oi, ol);
     KD_LAUNCH_CHECK();
+    mark(slot + 3, 1);
   }
   return KD_OK;
 }
@@ -648,14 +682,48 @@ int32_t kd_topk_kl_fwd_bwd_timed(const void* hidden, const void* W, int32_t in_d
                       grad_hidden, grad_W, row_lse, row_kl, workspace, workspace_bytes, status_dev, stream, events);
 }
 
+static int32_t fwd_impl(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                        const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                        float tau, int64_t chunk, float* loss, float* row_lse, float* row_kl, void* workspace,
+                        size_t workspace_bytes, int32_t* status_dev, void* stream, void* const* events) {
+  if (!hidden || !W || !teacher_idx || !teacher_logit || !loss || !row_lse) return KD_ERR_NULL_ARG;
+  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, loss, row_lse, row_kl, nullptr, nullptr, KD_F32,
+             nullptr, 0, nullptr, status_dev, (hipStream_t)stream, events};
+  return kd::dispatch(kd::kForward, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
+}
+
 int32_t kd_topk_kl_fwd(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
                        const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
                        float tau, int64_t chunk, float* loss, float* row_lse, float* row_kl, void* workspace,
                        size_t workspace_bytes, int32_t* status_dev, void* stream) {
-  if (!hidden || !W || !teacher_idx || !teacher_logit || !loss || !row_lse) return KD_ERR_NULL_ARG;
-  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, loss, row_lse, row_kl, nullptr, nullptr, KD_F32,
-             nullptr, 0, nullptr, status_dev, (hipStream_t)stream, nullptr};
-  return kd::dispatch(kd::kForward, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
+  return fwd_impl(hidden, W, in_dtype, teacher_idx, teacher_logit, mask, T, d, V, K, tau, chunk, loss, row_lse,
+                  row_kl, workspace, workspace_bytes, status_dev, stream, nullptr);
+}
+
+int32_t kd_topk_kl_fwd_timed(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                             const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
+                             int64_t K, float tau, int64_t chunk, float* loss, float* row_lse, float* row_kl,
+                             void* workspace, size_t workspace_bytes, int32_t* status_dev, void* stream,
+                             void* const* events) {
+  if (!events) return KD_ERR_NULL_ARG;
+  return fwd_impl(hidden, W, in_dtype, teacher_idx, teacher_logit, mask, T, d, V, K, tau, chunk, loss, row_lse,
+                  row_kl, workspace, workspace_bytes, status_dev, stream, events);
+}
+
+static int32_t bwd_impl(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                        const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                        float tau, int64_t chunk, const float* row_lse, const float* grad_loss, void* grad_hidden,
+                        int32_t grad_hidden_dtype, float* grad_W, int32_t accumulate_grad_W, uint16_t* grad_W_bf16,
+                        void* workspace, size_t workspace_bytes, int32_t* status_dev, void* stream,
+                        void* const* events) {
+  if (!hidden || !W || !teacher_idx || !teacher_logit || !row_lse) return KD_ERR_NULL_ARG;
+  if (!grad_hidden && !grad_W) return KD_ERR_NULL_ARG;
+  if (grad_W_bf16 && !grad_W) return KD_ERR_NULL_ARG;
+  if (grad_hidden_dtype != KD_F32 && grad_hidden_dtype != KD_BF16) return KD_ERR_DTYPE;
+  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, nullptr, const_cast<float*>(row_lse), nullptr,
+             grad_loss, grad_hidden, grad_hidden_dtype, grad_W, accumulate_grad_W ? 1 : 0, grad_W_bf16, status_dev,
+             (hipStream_t)stream, events};
+  return kd::dispatch(kd::kBackward, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
 }
 
 int32_t kd_topk_kl_bwd(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
@@ -663,14 +731,21 @@ int32_t kd_topk_kl_bwd(const void* hidden, const void* W, int32_t in_dtype, cons
                        float tau, int64_t chunk, const float* row_lse, const float* grad_loss, void* grad_hidden,
                        int32_t grad_hidden_dtype, float* grad_W, int32_t accumulate_grad_W, uint16_t* grad_W_bf16,
                        void* workspace, size_t workspace_bytes, int32_t* status_dev, void* stream) {
-  if (!hidden || !W || !teacher_idx || !teacher_logit || !row_lse) return KD_ERR_NULL_ARG;
-  if (!grad_hidden && !grad_W) return KD_ERR_NULL_ARG;
-  if (grad_W_bf16 && !grad_W) return KD_ERR_NULL_ARG;
-  if (grad_hidden_dtype != KD_F32 && grad_hidden_dtype != KD_BF16) return KD_ERR_DTYPE;
-  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, nullptr, const_cast<float*>(row_lse), nullptr,
-             grad_loss, grad_hidden, grad_hidden_dtype, grad_W, accumulate_grad_W ? 1 : 0, grad_W_bf16, status_dev,
-             (hipStream_t)stream, nullptr};
-  return kd::dispatch(kd::kBackward, in_dtype, T, d, V, K, chunk, workspace, workspace_bytes, a);
+  return bwd_impl(hidden, W, in_dtype, teacher_idx, teacher_logit, mask, T, d, V, K, tau, chunk, row_lse, grad_loss,
+                  grad_hidden, grad_hidden_dtype, grad_W, accumulate_grad_W, grad_W_bf16, workspace,
+                  workspace_bytes, status_dev, stream, nullptr);
+}
+
+int32_t kd_topk_kl_bwd_timed(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                             const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
+                             int64_t K, float tau, int64_t chunk, const float* row_lse, const float* grad_loss,
+                             void* grad_hidden, int32_t grad_hidden_dtype, float* grad_W, int32_t accumulate_grad_W,
+                             uint16_t* grad_W_bf16, void* workspace, size_t workspace_bytes, int32_t* status_dev,
+                             void* stream, void* const* events) {
+  if (!events) return KD_ERR_NULL_ARG;
+  return bwd_impl(hidden, W, in_dtype, teacher_idx, teacher_logit, mask, T, d, V, K, tau, chunk, row_lse, grad_loss,
+                  grad_hidden, grad_hidden_dtype, grad_W, accumulate_grad_W, grad_W_bf16, workspace,
+                  workspace_bytes, status_dev, stream, events);
 }
 
 size_t kd_topk_cache_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
@@ -679,9 +754,9 @@ size_t kd_topk_cache_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K,
   return p.total;
 }
 
-int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype, int64_t T, int64_t d, int64_t V,
-                            int64_t K, int64_t chunk, int32_t* out_idx, float* out_logit, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+static int32_t cache_impl(const void* hidden, const void* W, int32_t in_dtype, int64_t T, int64_t d, int64_t V,
+                          int64_t K, int64_t chunk, int32_t* out_idx, float* out_logit, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events) {
   if (!hidden || !W || !out_idx || !out_logit) return KD_ERR_NULL_ARG;
   kd::CachePlan p;
   const int32_t st = kd::make_cache_plan(T, d, V, K, chunk, in_dtype, &p);
@@ -689,8 +764,24 @@ int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype,
   if ((((uintptr_t)hidden) | ((uintptr_t)W)) & 15) return KD_ERR_BAD_SHAPE;
   if (!workspace || workspace_bytes < p.total || (((uintptr_t)workspace) & 255)) return KD_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (in_dtype == KD_BF16) return kd::run_cache<kd::Bf16>(p, hidden, W, out_idx, out_logit, (char*)workspace, s);
-  return kd::run_cache<kd::F32>(p, hidden, W, out_idx, out_logit, (char*)workspace, s);
+  if (in_dtype == KD_BF16)
+    return kd::run_cache<kd::Bf16>(p, hidden, W, out_idx, out_logit, (char*)workspace, s, events);
+  return kd::run_cache<kd::F32>(p, hidden, W, out_idx, out_logit, (char*)workspace, s, events);
+}
+
+int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype, int64_t T, int64_t d, int64_t V,
+                            int64_t K, int64_t chunk, int32_t* out_idx, float* out_logit, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return cache_impl(hidden, W, in_dtype, T, d, V, K, chunk, out_idx, out_logit, workspace, workspace_bytes, stream,
+                    nullptr);
+}
+
+int32_t kd_topk_cache_build_timed(const void* hidden, const void* W, int32_t in_dtype, int64_t T, int64_t d,
+                                  int64_t V, int64_t K, int64_t chunk, int32_t* out_idx, float* out_logit,
+                                  void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return KD_ERR_NULL_ARG;
+  return cache_impl(hidden, W, in_dtype, T, d, V, K, chunk, out_idx, out_logit, workspace, workspace_bytes, stream,
+                    events);
 }
 
 int32_t kd_mfma_probe(int32_t blocks, int32_t iters, int32_t zero_operands, float* out, void* stream) {

@@ -200,6 +200,20 @@ int32_t kd_topk_kl_fwd(const void* hidden, const void* W, int32_t in_dtype,
                        int32_t* status_dev, void* stream);
 
 /*
+ * kd_topk_kl_fwd with timing markers, for measurement: `events` as for
+ * kd_topk_kl_fwd_bwd_timed (phases 0-2 of every chunk carry the forward's
+ * launches; phases 3-7 are recorded as empty intervals).  KD_ERR_NULL_ARG
+ * if events is NULL.
+ */
+int32_t kd_topk_kl_fwd_timed(const void* hidden, const void* W, int32_t in_dtype,
+                             const int32_t* teacher_idx, const float* teacher_logit,
+                             const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                             float tau, int64_t chunk,
+                             float* loss, float* row_lse, float* row_kl,
+                             void* workspace, size_t workspace_bytes,
+                             int32_t* status_dev, void* stream, void* const* events);
+
+/*
  * Backward only: the gradients of g * loss, with g = *grad_loss (device fp32
  * scalar; NULL means 1), recomputing every chunk's logits.
  *  row_lse            device [T] fp32 from kd_topk_kl_fwd on the same inputs.
@@ -225,6 +239,23 @@ int32_t kd_topk_kl_bwd(const void* hidden, const void* W, int32_t in_dtype,
                        float* grad_W, int32_t accumulate_grad_W, uint16_t* grad_W_bf16,
                        void* workspace, size_t workspace_bytes,
                        int32_t* status_dev, void* stream);
+
+/*
+ * kd_topk_kl_bwd with timing markers, for measurement: `events` as for
+ * kd_topk_kl_fwd_bwd_timed (phase 0 carries the chunk's H^T copy, phases
+ * 3-7 the backward's launches; phases 1-2, and those of a gradient not
+ * asked for, are recorded as empty intervals).  KD_ERR_NULL_ARG if events
+ * is NULL.
+ */
+int32_t kd_topk_kl_bwd_timed(const void* hidden, const void* W, int32_t in_dtype,
+                             const int32_t* teacher_idx, const float* teacher_logit,
+                             const uint8_t* mask, int64_t T, int64_t d, int64_t V, int64_t K,
+                             float tau, int64_t chunk,
+                             const float* row_lse, const float* grad_loss,
+                             void* grad_hidden, int32_t grad_hidden_dtype,
+                             float* grad_W, int32_t accumulate_grad_W, uint16_t* grad_W_bf16,
+                             void* workspace, size_t workspace_bytes,
+                             int32_t* status_dev, void* stream, void* const* events);
 
 /*
  * Offline top-K teacher-logit cache: the record the loss reads as
@@ -256,6 +287,28 @@ int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype,
                             int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk,
                             int32_t* out_idx, float* out_logit,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of timed phases per chunk of the cache builder. */
+#define KD_CACHE_PHASES 4
+
+/*
+ * kd_topk_cache_build with timing markers, for measurement.  `events` points
+ * to 2 * (KD_CACHE_PHASES * nchunks + 1) hipEvent_t created by the caller
+ * (nchunks = ceil(T / min(chunk, T))); events[2*i] is recorded before and
+ * events[2*i + 1] after
+ *   i = c * KD_CACHE_PHASES + p   phase p of chunk c: 0 the first head GEMM
+ *       (per-row block maxima, after the chunk's padded copy if any),
+ *       1 the threshold selection, 2 the second head GEMM (candidates),
+ *       3 the sort of the candidates and the exact fallback;
+ *   i = KD_CACHE_PHASES * nchunks  the prologue (padded copy of W, if any).
+ * Everything else is as for kd_topk_cache_build; KD_ERR_NULL_ARG if events
+ * is NULL.
+ */
+int32_t kd_topk_cache_build_timed(const void* hidden, const void* W, int32_t in_dtype,
+                                  int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                                  int32_t* out_idx, float* out_logit,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  void* const* events);
 
 /*
  * Measurement only (not part of the loss): the sustained bf16 MFMA ceiling.

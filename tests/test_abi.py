@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
                                           "kd_topk_kl_fwd_workspace_bytes", "kd_topk_kl_bwd_workspace_bytes",
                                           "kd_topk_kl_dw_chunks", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
                                           "kd_topk_cache_workspace_bytes", "kd_topk_cache_build",
-                                          "kd_mfma_probe"}
+                                          "kd_mfma_probe", "kd_topk_kl_fwd_timed", "kd_topk_kl_bwd_timed",
+                                          "kd_topk_cache_build_timed"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -198,3 +199,22 @@ def test_mfma_probe_host_errors():
     assert L.kd_mfma_probe(1, 1, 0, None, None) == 1                          # NULL out
     assert L.kd_mfma_probe(0, 1, 0, ctypes.c_void_p(0x10000), None) == 2     # no blocks
     assert L.kd_mfma_probe(1, 0, 0, ctypes.c_void_p(0x10000), None) == 2     # no iterations
+
+
+def test_timed_entry_points_require_events():
+    L = kd.lib()
+    v = ctypes.c_void_p
+    p = v(0x10000)
+    assert L.kd_topk_kl_fwd_timed(p, p, 0, p, p, None, 64, 64, 1000, 10, 1.0, 32, p, p, None, p, 1 << 40,
+                                  None, None, None) == 1
+    assert L.kd_topk_kl_bwd_timed(p, p, 0, p, p, None, 64, 64, 1000, 10, 1.0, 32, p, None, p, 1, p, 0, None,
+                                  p, 1 << 40, None, None, None) == 1
+    assert L.kd_topk_cache_build_timed(p, p, 0, 64, 64, 1000, 10, 32, p, p, p, 1 << 40, None, None) == 1
+
+
+def test_header_constants_match_the_binding():
+    src = open(HEADER).read()
+    for name, val in (("KD_NUM_PHASES", kd.KD_NUM_PHASES), ("KD_CACHE_PHASES", kd.KD_CACHE_PHASES),
+                      ("KD_BF16", kd.KD_BF16), ("KD_F32", kd.KD_F32)):
+        assert re.search(rf"#define {name} (\d+)", src).group(1) == str(val), name
+    assert len(kd.PHASES) == kd.KD_NUM_PHASES and len(kd.CACHE_PHASES) == kd.KD_CACHE_PHASES

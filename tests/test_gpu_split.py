@@ -151,3 +151,31 @@ def test_autograd_end_to_end(dtype):
     e_acc = rel_f(acc.cpu().numpy(), 2 * ref["grad_W"])
     log(f"[gpu-split] accumulator relF {e_acc:.2e}")
     assert e_acc <= GRAD_TOL
+
+
+def test_timed_split_calls_match_untimed():
+    """The measurement entry points (events around every phase) give the
+    same bits as the plain calls."""
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    x = _inputs(3, 520, d=256, V=3000, seed=13)
+    t = to_device(x)
+    args = (t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"])
+    log("[gpu-split] timed split calls")
+    nslots = kd.KD_NUM_PHASES * (-(-520 // 128)) + 2
+
+    def events():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nslots)]
+        for e in ev:
+            e.record()
+        return ev
+
+    loss_a, rl_a = kd.fwd(*args, tau=x["tau"], chunk=128)
+    loss_b, rl_b = kd.fwd(*args, tau=x["tau"], chunk=128, events=events())
+    gH_a, gW_a, _ = kd.bwd(*args, rl_a, tau=x["tau"], chunk=128)
+    eb = events()
+    gH_b, gW_b, _ = kd.bwd(*args, rl_b, tau=x["tau"], chunk=128, events=eb)
+    torch.cuda.synchronize()
+    assert float(loss_a.item()) == float(loss_b.item()) and torch.equal(rl_a, rl_b)
+    assert torch.equal(gH_a, gH_b) and torch.equal(gW_a, gW_b)
+    assert all(eb[2 * i].elapsed_time(eb[2 * i + 1]) >= 0 for i in range(nslots))

@@ -165,3 +165,21 @@ def test_cache_feeds_the_loss():
     assert rel(float(loss.item()), ref["loss"]) <= LOSS_TOL
     assert rel_f(gH.cpu().numpy(), ref["grad_hidden"]) <= GRAD_TOL
     assert rel_f(gW.cpu().numpy(), ref["grad_W"]) <= GRAD_TOL
+
+
+def test_timed_build_matches_untimed():
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    rng = np.random.default_rng(9)
+    H = _dev(_bf16(rng.standard_normal((100, 128))), "bf16")
+    W = _dev(_bf16(rng.standard_normal((3000, 128)) * 0.1), "bf16")
+    log("[gpu-cache] timed build")
+    nslots = kd.KD_CACHE_PHASES * (-(-100 // 32)) + 1
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nslots)]
+    for e in ev:
+        e.record()
+    a = kd.topk_cache(H, W, K=16, chunk=32)
+    b = kd.topk_cache(H, W, K=16, chunk=32, events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert all(ev[2 * i].elapsed_time(ev[2 * i + 1]) >= 0 for i in range(nslots))
