@@ -20,7 +20,7 @@ KD_F32 = 1
 KD_NUM_PHASES = 8
 KD_CACHE_PHASES = 4
 CACHE_PHASES = ("gemm_block_max", "threshold", "gemm_collect", "select")
-PHASES = ("chunk_prep", "gemm_fwd_lse", "kl_rows", "gemm_bwd_grad", "scatter_sparse",
+PHASES = ("chunk_prep", "gemm_fwd_lse", "kl_rows", "gemm_bwd_grad", "teacher_p",
           "gemm_dhidden", "dhidden_reduce", "gemm_dW")
 STATUS = {0: "KD_OK", 1: "KD_ERR_NULL_ARG", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_TAU",
           4: "KD_ERR_BAD_CHUNK", 5: "KD_ERR_DTYPE", 6: "KD_ERR_WORKSPACE",

@@ -153,8 +153,7 @@ __device__ const uint8_t kMaskAll = 1;
 // fused call), written in two layouts (G [R_p][V_p] and G^T [V_p][R_p]) for
 // the two gradient GEMMs; entries at v >= V are unused.  The sparse teacher
 // part -g (tau/N) m_t P[t,v] is subtracted in the epilogue from the fp32
-// values (fused call, through the forward's hit lists) or afterwards by
-// scatter_sparse_kernel (backward-only call).
+// values, through the chunk's hit lists, before G is rounded.
 template <class E>
 struct EpiGrad {
   typename E::T* G;
@@ -168,9 +167,8 @@ struct EpiGrad {
   const float* grad_loss; // device scalar g, or nullptr for 1
   float tau, c2;
   int V, R;
-  // The sparse teacher part in the epilogue (fused call): the forward's
-  // teacher-id hit lists and the teacher probabilities psel[t*K + k]; with
-  // hit_off == nullptr it is left to scatter_sparse_kernel.
+  // The sparse teacher part: the chunk's teacher-id hit lists and the
+  // teacher probabilities psel[t*K + k] (hit_off == nullptr: left out).
   const int* hit_off;
   const uint2* hits;
   const float* psel;
@@ -608,6 +606,10 @@ __global__ __launch_bounds__(1024) void prep_kernel(const uint8_t* mask, int64_t
   }
 }
 
+__global__ __launch_bounds__(256) void fill_i32_kernel(int* p, int64_t n, int v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
 // Teacher-id hit lists of a chunk, filed by forward-GEMM wave tile: one
 // block per 64-row group g of the chunk sorts the group's (t, k) entries by
 // vocabulary strip id / kHitV (counting sort in LDS: count, scan, fill).
@@ -617,10 +619,6 @@ __global__ __launch_bounds__(1024) void prep_kernel(const uint8_t* mask, int64_t
 // in any order; each names its own output slot, so results do not depend on
 // it.  Groups past the chunk's rows (up to the GEMM tiles' extent) get empty
 // lists.  Dynamic LDS: nvt + 1 ints.
-__global__ __launch_bounds__(256) void fill_i32_kernel(int* p, int64_t n, int v) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
-}
-
 __global__ __launch_bounds__(1024) void hit_build_kernel(const int32_t* idx, int R, int K, int V, int nvt, int* off,
                                                          uint2* hits) {
   extern __shared__ int s_h[];
@@ -851,45 +849,23 @@ __global__ __launch_bounds__(256) void chunk_loss_kernel(const double* rowkl, co
   if (threadIdx.x == 0) *loss_acc += s;
 }
 
-// Sparse teacher part of the logit gradient: G[t, id] -= g (tau/N) m_t
-// P[t, id] for every distinct valid id of the row (duplicates summed first),
-// in both gradient layouts.  One block per chunk row.  Invalid ids set
-// *status if status is not NULL (the backward-only call; otherwise the
-// forward's KL kernel reports them).
-template <class E>
-__global__ __launch_bounds__(128) void scatter_sparse_kernel(
-    const int32_t* idx, const float* logit, const uint8_t* mask, int K, int V, float tau, const int* count,
-    const float* grad_loss, typename E::T* G, int64_t ldg, typename E::T* Gt, int64_t ldgt, int32_t* status) {
+// Teacher probabilities p_k of the chunk's rows for the recompute epilogue's
+// sparse part, in the backward-only call (the fused call gets them from
+// kl_rows_kernel).  One block per chunk row; invalid ids set *status and are
+// left out of the hit lists, so they contribute nothing.
+__global__ __launch_bounds__(128) void teacher_p_kernel(const int32_t* idx, const float* logit, int K, int V,
+                                                        float tau, float* psel, int32_t* status) {
   __shared__ float s_a[kMaxK];
-  __shared__ int s_id[kMaxK];
   __shared__ float s_red[128];
   const int t = blockIdx.x;
-  if (status) {
-    for (int k = threadIdx.x; k < K; k += 128) {
-      const int id = idx[(int64_t)t * K + k];
-      if (id < 0 || id >= V) *status = 7;   // KD_ERR_BAD_INDEX
-    }
-  }
-  if (*count == 0 || (mask && !mask[t])) return;
-  const float s = grad_scale(count, grad_loss, tau);
-  const float inv_tau = 1.f / tau;
-  for (int k = threadIdx.x; k < K; k += 128) s_id[k] = idx[(int64_t)t * K + k];
-  const float lse_a = teacher_row<128>(logit + (int64_t)t * K, K, inv_tau, s_a, s_red);
-  __syncthreads();
+  const float lse_a = teacher_row<128>(logit + (int64_t)t * K, K, 1.f / tau, s_a, s_red);
   for (int k = threadIdx.x; k < K; k += 128) {
-    const int id = s_id[k];
-    if (id < 0 || id >= V) continue;
-    bool first = true;
-    for (int k2 = 0; k2 < k; ++k2)
-      if (s_id[k2] == id) { first = false; break; }
-    if (!first) continue;
-    float P = 0.f;
-    for (int k2 = k; k2 < K; ++k2)
-      if (s_id[k2] == id) P += expf(s_a[k2] - lse_a);
-    typename E::T* g = G + (int64_t)t * ldg + id;
-    const typename E::T nv = store_cvt<E>(load_elem<E>(g) - s * P);
-    *g = nv;
-    Gt[(int64_t)id * ldgt + t] = nv;
+    const int id = idx[(int64_t)t * K + k];
+    if (id < 0 || id >= V) {
+      if (status) *status = 7;                // KD_ERR_BAD_INDEX
+      continue;
+    }
+    psel[(int64_t)t * K + k] = expf(s_a[k] - lse_a);
   }
 }
 

@@ -17,7 +17,7 @@
 //     chunk loss      fixed-order fp64 sum of m_t KL_t
 //     GEMM + grad     recompute z^T, G = (tau/N) m (q - P) in two layouts,
 //                     the sparse teacher part P at the hit lists' entries
-//   (the backward-only entry point subtracts P with a scatter kernel instead)
+//   (the backward-only entry point first recomputes the teacher's P)
 //     GEMM dH         split-K over the vocabulary, fixed-order reduction
 //     GEMM dW         grad_W (+)= G^T H in fp32, once per group of
 //                     consecutive chunks spanning >= 4096 rows (their G^T
@@ -128,9 +128,9 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
     return KD_ERR_BAD_SHAPE;
   if ((int64_t)kBM * P.V_p * P.eb >= (1ll << 32) || (int64_t)kBM * P.R_g * P.eb >= (1ll << 32))
     return KD_ERR_BAD_SHAPE;
-  // hit lists (forward): int32 entry indices; a row group's strip counts
-  // sit in 64 KB of LDS, so V_p / 128 + 1 <= 16384, i.e. V <= 2096896
-  if (P.R_p * K >= (1ll << 31) || (P.fwd && (P.nvt + 1) * 4 > 65536)) return KD_ERR_BAD_SHAPE;
+  // hit lists: int32 entry indices; a row group's strip counts sit in 64 KB
+  // of LDS, so V_p / 128 + 1 <= 16384, i.e. V <= 2096896
+  if (P.R_p * K >= (1ll << 31) || (P.nvt + 1) * 4 > 65536) return KD_ERR_BAD_SHAPE;
   // split-K of the hidden-gradient GEMM (output only chunk x d): pick the
   // split count whose grid fills whole waves of 256 CUs best, with at least
   // one full wave, and a small penalty per split for the partial-sum traffic.
@@ -168,11 +168,11 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   take(P.off_lse2, F, (size_t)P.R_p * sizeof(float));
   take(P.off_rowkl, F, (size_t)P.R_p * sizeof(double));
   take(P.off_dh, B, (size_t)P.splits * P.R_p * P.Nd_p * sizeof(float));
-  take(P.off_hoff, F, (size_t)P.nbt * (P.nvt + 1) * sizeof(int));
-  take(P.off_hits, F, (size_t)P.R_p * K * sizeof(uint2));
+  take(P.off_hoff, true, (size_t)P.nbt * (P.nvt + 1) * sizeof(int));
+  take(P.off_hits, true, (size_t)P.R_p * K * sizeof(uint2));
   take(P.off_zsel, F, (size_t)P.R_p * K * sizeof(float));
   take(P.off_part2, F, (size_t)P.ng * P.R_p * sizeof(float2));
-  take(P.off_psel, F && B, (size_t)P.R_p * K * sizeof(float));   // teacher p for the fused sparse part
+  take(P.off_psel, B, (size_t)P.R_p * K * sizeof(float));   // teacher p for the epilogue's sparse part
   P.total = o;
   return KD_OK;
 }
@@ -276,7 +276,7 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
   uint2* hits = (uint2*)(ws + P.off_hits);
   float* zsel = (float*)(ws + P.off_zsel);
   float2* part2 = (float2*)(ws + P.off_part2);
-  float* psel = (P.fwd && P.bwd) ? (float*)(ws + P.off_psel) : nullptr;
+  float* psel = P.bwd ? (float*)(ws + P.off_psel) : nullptr;
 
   const int64_t T_ = P.T, d = P.d, V = P.V, K = P.K;
   const float tau = A.tau;
@@ -334,12 +334,10 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
                           (unsigned)(P.d_p / 64), st);
       KD_LAUNCH_CHECK();
     }
-    if (P.fwd) {
-      // teacher-id hit lists for the forward epilogue
-      hipLaunchKernelGGL(hit_build_kernel, dim3((unsigned)(Rt / kHitT)), dim3(1024),
-                         (size_t)(P.nvt + 1) * sizeof(int), st, idx_c, R, (int)K, (int)V, (int)P.nvt, hoff, hits);
-      KD_LAUNCH_CHECK();
-    }
+    // teacher-id hit lists for the forward and the recompute epilogues
+    hipLaunchKernelGGL(hit_build_kernel, dim3((unsigned)(Rt / kHitT)), dim3(1024),
+                       (size_t)(P.nvt + 1) * sizeof(int), st, idx_c, R, (int)K, (int)V, (int)P.nvt, hoff, hits);
+    KD_LAUNCH_CHECK();
     mark(slot + 0, 1);
 
     if (P.fwd) {
@@ -370,6 +368,15 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       for (int p = 3; p < KD_NUM_PHASES; ++p) skip(slot + p);
       continue;
     }
+    // backward-only call: the teacher probabilities the forward's KL kernel
+    // would have left (phase 4, recorded ahead of phase 3)
+    mark(slot + 4, 0);
+    if (!P.fwd) {
+      hipLaunchKernelGGL(teacher_p_kernel, dim3(R), dim3(128), 0, st, idx_c, logit_c, (int)K, (int)V, tau, psel,
+                         A.status);
+      KD_LAUNCH_CHECK();
+    }
+    mark(slot + 4, 1);
 
     mark(slot + 3, 0);
     // backward recompute: G = (tau/N) m q, both layouts; the row normaliser
@@ -379,21 +386,12 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       const float* lse_src = P.fwd ? (const float*)lse2 : (const float*)A.row_lse + c0;
       const float lse_to2 = P.fwd ? 1.f : kLog2e;
       GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-      // fused call: the sparse teacher part goes in the epilogue
+      // the sparse teacher part goes in the epilogue, through the hit lists
       EpiGrad<E> epi{G, P.V_p, Gt + gslot * P.R_p, P.R_g, lse_src, lse_to2, mask_c, count, A.grad_loss, tau, c2,
-                     (int)V, R,
-                     psel ? hoff : nullptr, hits, psel, (int)(P.nvt + 1)};
+                     (int)V, R, hoff, hits, psel, (int)(P.nvt + 1)};
       if (launch_gemm<TileMain, E>(g, epi, st) != hipSuccess) return KD_ERR_HIP;
     }
     mark(slot + 3, 1);
-    mark(slot + 4, 0);
-    if (!psel) {
-      hipLaunchKernelGGL(scatter_sparse_kernel<E>, dim3(R), dim3(128), 0, st, idx_c, logit_c, mask_c, (int)K,
-                         (int)V, tau, (const int*)count, A.grad_loss, G, P.V_p, Gt + gslot * P.R_p, P.R_g,
-                         A.status);
-      KD_LAUNCH_CHECK();
-    }
-    mark(slot + 4, 1);
     if (want_dh) {
       mark(slot + 5, 0);
       // dH_c = G W  (A = G [Rt x V_p], B = W^T [d x V_p]), split-K over V

@@ -53,7 +53,7 @@ extern "C" {
 #define KD_ERR_NULL_ARG 1    /* a required pointer is NULL                      */
 #define KD_ERR_BAD_SHAPE 2   /* T, d, V or K < 1, K > V, K > KD_MAX_K, V*d,     */
                              /* chunk*V or T*d beyond what the kernels address, */
-                             /* or (loss, forward) V > 2096896                  */
+                             /* or (loss) V > 2096896                           */
 #define KD_ERR_BAD_TAU 3     /* tau <= 0 or not finite                          */
 #define KD_ERR_BAD_CHUNK 4   /* chunk < 1                                       */
 #define KD_ERR_DTYPE 5       /* in_dtype is not KD_BF16 or KD_F32               */
@@ -145,8 +145,10 @@ int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype,
  *       0 zero-padded H_c and H_c^T and the teacher-id hit lists,
  *       1 forward GEMM with the logsumexp partials and the logits at the
  *       teacher ids, 2 logsumexp merge, KL rows and the chunk's loss sum,
- *       3 recompute GEMM with the gradient epilogue, 4 sparse teacher
- *       scatter, 5 hidden-gradient GEMM, 6 its split-K reduction,
+ *       3 recompute GEMM with the gradient epilogue, 4 the teacher
+ *       probabilities of the backward-only call (recorded ahead of phase 3;
+ *       empty in the fused call), 5 hidden-gradient GEMM, 6 its split-K
+ *       reduction,
  *       7 head-gradient GEMM (launched in the last chunk of each group of
  *       kd_topk_kl_dw_chunks(...) chunks; empty in the group's others);
  *   i = KD_NUM_PHASES * nchunks      the prologue (count N, W^T);

@@ -51,7 +51,7 @@ def test_workspace_bytes_validation_and_scaling():
     # the forward's hit-list strip counts fit 64 KB of LDS up to V = 2096896
     assert wb(64, 64, 2096896, 10, 64, 0) > 0 and wb(64, 64, 2096897, 10, 64, 0) == 0
     assert kd.fwd_workspace_bytes(64, 64, 2096897, 10, 64, 0) == 0
-    assert kd.bwd_workspace_bytes(64, 64, 2096897, 10, 64, 0) > 0       # the backward builds no hit lists
+    assert kd.bwd_workspace_bytes(64, 64, 2096897, 10, 64, 0) == 0      # the backward builds them too
     # independent of T beyond the chunk
     a = wb(32768, 2880, 201088, 100, 4096, 0)
     b = wb(262144, 2880, 201088, 100, 4096, 0)

@@ -99,7 +99,7 @@ def test_maximum_vocabulary():
 
 def test_maximum_cache_width():
     """K = KD_MAX_K = 4096 ids per row (with a duplicate), fused and split
-    backward (whose sparse scatter merges duplicates in LDS)."""
+    backward (whose hit lists then hold 64 K entries per row group)."""
     import torch
     import chunked_top_kl_lm_amd as kd
     from tests.gpu_util import to_device
