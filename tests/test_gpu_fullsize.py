@@ -12,7 +12,8 @@ vocabulary, so these tests check:
   - the workspace and the peak device memory beyond the O(T) buffers do not
     depend on T.
 The reduced-T tests in test_gpu_parity.py check grad_W element by element at
-these d and V.
+these d and V.  At the 32K workload the split calls are checked against the
+fused call, and the cache builder's sampled rows against the oracle.
 """
 import numpy as np
 import pytest
@@ -88,6 +89,57 @@ def _checks(x, cfg, out, n_random=6):
 def test_gptoss_32k_full():
     x, cfg, out = _run_full(3)
     _checks(x, cfg, out)
+    # the split calls at the same size (bench.py --split): the forward's loss
+    # and row statistics are the fused call's bit for bit, the gradients equal
+    # them up to the rounding of the saved natural-log normaliser
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    t = out["t"]
+    args = (t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"])
+    log("[gpu-full] workload 3 through the split calls")
+    loss_s, rl_s = kd.fwd(*args, tau=cfg.tau, chunk=cfg.chunk)
+    gH_s, gW_s, _ = kd.bwd(*args, rl_s, tau=cfg.tau, chunk=cfg.chunk)
+    torch.cuda.synchronize()
+    assert float(loss_s.item()) == out["loss"]
+    assert np.array_equal(rl_s.cpu().numpy(), out["row_lse"])
+    e_h = float(torch.linalg.norm(gH_s - out["gH"]) / torch.linalg.norm(out["gH"]))
+    e_w = float(torch.linalg.norm(gW_s - out["gW"]) / torch.linalg.norm(out["gW"]))
+    log(f"[gpu-full] split vs fused: dH relF {e_h:.2e}  dW relF {e_w:.2e}")
+    assert e_h < 1e-3 and e_w < 1e-3
+
+
+def test_topk_cache_full_size_sampled_rows():
+    """The cache builder at the full 32K head (bench.py --topk-cache): every
+    row valid and sorted, and sampled rows against the oracle's fp64 logits."""
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    from oracle import teacher_logits, topk_cache
+    cfg = config_for(3)
+    log("[gpu-full] generating the 32K head for the cache builder")
+    x = make_inputs(cfg, seed=0, topk_backend="torch-cuda")
+    t = to_device(x)
+    idx, logit = kd.topk_cache(t["hidden"], t["W"], K=cfg.K, chunk=cfg.chunk)
+    torch.cuda.synchronize()
+    idx, logit = idx.cpu().numpy(), logit.cpu().numpy()
+    V = cfg.V
+    assert idx.min() >= 0 and idx.max() < V
+    assert np.all(np.diff(logit, axis=1) <= 0)
+    rows = [0, 1, cfg.T // 2, cfg.T - 1] + np.random.default_rng(5).integers(0, cfg.T, 8).tolist()
+    log(f"[gpu-full] cache rows {rows}")
+    H = x["hidden"][rows]
+    z = teacher_logits(H, x["W"])
+    ref_idx, ref_val = topk_cache(H, x["W"], cfg.K)
+    for i, r in enumerate(rows):
+        ids = idx[r]
+        assert len(set(ids.tolist())) == cfg.K
+        tol = 1e-5 * max(1.0, np.abs(z[i]).max())
+        assert np.abs(logit[r] - z[i, ids]).max() <= tol
+        out_mask = np.ones(V, dtype=bool)
+        out_mask[ids] = False
+        assert z[i, ids].min() >= z[i, out_mask].max() - 2 * tol
+        gap = ref_val[i, cfg.K - 1] - np.sort(z[i])[::-1][cfg.K]
+        if gap > 4 * tol:
+            assert sorted(ids.tolist()) == sorted(ref_idx[i].tolist())
 
 
 def test_long_128k_full_tau2():
