@@ -12,7 +12,8 @@ Prints ONE JSON line.  Extra keys: roofline (dominant kernel, live HIP-event
 timing inside the timed region), cpu_baseline (the fp64 oracle on a bounded
 sample of the same workload, host cores), mfma_ceiling (an MFMA-only loop on
 random operands timed after the step: what the MFMA pipes deliver at the
-clock the chip sustains), phases_ms, peak_gib.
+clock the chip sustains), phases_ms, peak_gib; with --library-gemm also
+library_gemm (torch.matmul on the same contraction shapes, a calibration).
 """
 from __future__ import annotations
 
@@ -102,6 +103,40 @@ def mfma_ceiling(kd, torch, dev, reps: int = 3) -> float:
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
     return blocks * 8 * 64 * iters * 32768.0 / (ms * 1e-3) / 1e12
+
+
+def library_gemm(torch, dev, rows: int, d: int, V: int, rows_dw: int, reps: int = 10) -> dict:
+    """The vendor GEMM library (torch.matmul, bf16 in, fp32 accumulate, bf16
+    out) on the step's contraction shapes, as a calibration of the GEMM
+    kernels: logits [rows x d][d x V] (the forward and recompute shape),
+    hidden gradient [rows x V][V x d], head gradient [V x rows_dw][rows_dw x d].
+    Plain products: none of the epilogue work (logsumexp, gradient, fp32
+    accumulation into grad_W) is in these times."""
+    g = torch.Generator(device=dev).manual_seed(1)
+    bf = torch.bfloat16
+    H = torch.randn(rows, d, device=dev, dtype=bf, generator=g)
+    W = torch.randn(V, d, device=dev, dtype=bf, generator=g) * 0.02
+    G = torch.randn(rows, V, device=dev, dtype=bf, generator=g) * 1e-3
+    Gt = torch.randn(V, rows_dw, device=dev, dtype=bf, generator=g) * 1e-3
+    Hg = torch.randn(rows_dw, d, device=dev, dtype=bf, generator=g)
+    cases = {"logits": (lambda: H @ W.t(), 2.0 * rows * d * V),
+             "dhidden": (lambda: G @ W, 2.0 * rows * d * V),
+             "dW": (lambda: Gt @ Hg, 2.0 * rows_dw * d * V)}
+    out = {}
+    for name, (f, fl) in cases.items():
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[name] = {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12}
+    out["shapes"] = {"logits": [rows, d, V], "dhidden": [rows, V, d], "dW": [V, rows_dw, d]}
+    return out
 
 
 def load_traffic(kernel: str, workload: str, path: str = None):
@@ -279,6 +314,8 @@ def main() -> int:
                     help="time the split entry points (forward call, then backward call) instead of the fused call")
     ap.add_argument("--topk-cache", action="store_true",
                     help="measure the offline top-K cache builder on the workload's head instead of the loss")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch.matmul on the step's contraction shapes (a calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/pmc_traffic.json from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
@@ -436,6 +473,14 @@ def main() -> int:
         "input_gen_s": t_gen,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if args.library_gemm and dt == kd.KD_BF16:
+        lib = library_gemm(torch, dev, min(chunk, T), d, V, kd.dw_chunks(T, d, V, K, chunk, dt) * min(chunk, T))
+        ndw = -(-nchunks // kd.dw_chunks(T, d, V, K, chunk, dt))
+        lib["ours_ms_per_launch"] = {"logits (forward)": phase_ms["gemm_fwd_lse"] / nchunks,
+                                     "logits (recompute)": phase_ms["gemm_bwd_grad"] / nchunks,
+                                     "dhidden": phase_ms["gemm_dhidden"] / nchunks,
+                                     "dW": phase_ms["gemm_dW"] / ndw}
+        res["library_gemm"] = lib
     if not args.no_cpu_baseline:
         del t, ws, out
         torch.cuda.empty_cache()
