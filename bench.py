@@ -1,11 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of the fused chunked top-K KL loss (forward + backward) on one MI355X.
 
-One step = one call of the whole hot path (count, W^T, and per chunk: forward
-GEMM with the online logsumexp, KL at the teacher ids, recompute GEMM with the
-gradient epilogue, sparse scatter, hidden-gradient GEMM, head-gradient GEMM;
-then the final loss) over one batch of synthetic inputs already resident in
-HBM.  Default workload: T=32768, d=2880, V=201088, K=100, chunk=2048, tau=1,
+One step = one call of the whole hot path (count, W^T, and per chunk: the
+teacher ids filed per tile, forward GEMM with the online logsumexp and the
+logits at the teacher ids, KL, recompute GEMM with the softmax-minus-sparse-
+target gradient epilogue, hidden-gradient GEMM, head-gradient GEMM; then the
+final loss) over one batch of synthetic inputs already resident in HBM.  Default workload: T=32768, d=2880, V=201088, K=100, chunk=2048, tau=1,
 bf16 hidden/W (a gpt-oss-20b-sized output head at 32K context).
 
 Prints ONE JSON line.  Extra keys: roofline (dominant kernel, live HIP-event

@@ -571,7 +571,8 @@ struct OpAddI { __device__ int operator()(int a, int b) const { return a + b; } 
 
 // Teacher distribution of one row: a_k = logit_k / tau kept in s_a, and the
 // log normaliser log sum_k exp(a_k).  p_k = exp(a_k - lse_a).  Used by both
-// the KL kernel and the sparse scatter so that both see the same p.
+// the KL kernel and the teacher-probability kernel of the backward-only call,
+// so that the loss and the gradient see the same p.
 template <int NT>
 __device__ __forceinline__ float teacher_row(const float* logit_row, int K, float inv_tau,
                                              float* s_a, float* s_red) {
