@@ -12,15 +12,25 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+def _host_tensor(a: np.ndarray):
+    """A torch view of a host array that is only read (copied to the device):
+    read-only arrays (cached inputs) are wrapped without a host copy."""
+    import warnings
+    import torch
+    with warnings.catch_warnings():
+        warnings.filterwarnings("ignore", message="The given NumPy array is not writable")
+        return torch.from_numpy(a)
+
+
 def to_device(x: dict):
     import torch
     dev = torch.device("cuda:0")
     if x["dtype"] == "bf16":
-        h = torch.from_numpy(np.asarray(x["hidden"]).view(np.int16)).view(torch.bfloat16)
-        w = torch.from_numpy(np.asarray(x["W"]).view(np.int16)).view(torch.bfloat16)
+        h = _host_tensor(np.asarray(x["hidden"]).view(np.int16)).view(torch.bfloat16)
+        w = _host_tensor(np.asarray(x["W"]).view(np.int16)).view(torch.bfloat16)
     else:
-        h = torch.from_numpy(np.asarray(x["hidden"]))
-        w = torch.from_numpy(np.asarray(x["W"]))
+        h = _host_tensor(np.asarray(x["hidden"]))
+        w = _host_tensor(np.asarray(x["W"]))
     return dict(hidden=h.to(dev), W=w.to(dev),
                 teacher_idx=torch.from_numpy(x["teacher_idx"]).to(dev),
                 teacher_logit=torch.from_numpy(x["teacher_logit"]).to(dev),

@@ -1,7 +1,7 @@
 """Full-size workloads on the GPU, in the launch configuration bench.py times.
 
-At T = 32768 / 131072 / 262144 the oracle cannot form every row's full
-vocabulary, so these tests check:
+At T = 8192 / 32768 / 131072 / 262144 the oracle cannot form every row's
+full vocabulary in seconds, so these tests check:
   - sampled rows (first, last, masked, random) of row_lse, row_kl and
     grad_hidden against the oracle's per-row results, element by element;
   - the loss against tau^2 * sum_t m_t KL_t / N recomputed in fp64 from the
@@ -84,6 +84,11 @@ def _checks(x, cfg, out, n_random=6):
     log(f"[gpu-full] column-sum ratio {cs:.2e}  <dH,H> {a:.6e}  <dW,W> {b:.6e}")
     assert cs < 1e-2
     assert rel(a, b) < GRAD_TOL
+
+
+def test_llama_8k_full():
+    x, cfg, out = _run_full(2)
+    _checks(x, cfg, out)
 
 
 def test_gptoss_32k_full():
