@@ -50,12 +50,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even, NaN kept NaN (quiet bit set, payload
+// truncated).  gfx950 has this as v_cvt_pk_bf16_f32, two values per
+// instruction; over all 2^32 fp32 bit patterns its results equal the integer
+// form ((u + 0x7fff + bit 16 of u) >> 16, NaN: (u >> 16) | 0x40) bit for bit.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <class E> __device__ __forceinline__ float load_elem(const typename E::T* p);

@@ -330,10 +330,8 @@ struct EpiGrad {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int vl0 = 32 * i + 8 * g4 + 4 * (c.lane >> 5);
-          uint16_t b[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16(acc[i][j][4 * g4 + e]);
-          pk[i][j][g4] = make_uint2((uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16));
+          pk[i][j][g4] = make_uint2(pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]),
+                                    pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]));
           *(uint2*)(lds + tl * 256 + (((vl0 >> 3) ^ (tl & 15)) << 4) + ((vl0 & 7) << 1)) = pk[i][j][g4];
         }
     }
@@ -376,8 +374,8 @@ struct EpiGrad {
 
   __device__ __forceinline__ static void store4(uint16_t* p, const float* g) {
     uint2 w;
-    w.x = (uint32_t)f32_to_bf16(g[0]) | ((uint32_t)f32_to_bf16(g[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16(g[2]) | ((uint32_t)f32_to_bf16(g[3]) << 16);
+    w.x = pack_bf16x2(g[0], g[1]);
+    w.y = pack_bf16x2(g[2], g[3]);
     *(uint2*)p = w;
   }
   __device__ __forceinline__ static void store4(float* p, const float* g) {
@@ -893,8 +891,7 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* part, int64
 // per split, same fixed summation order.
 __device__ __forceinline__ void store_out4(float* p, float4 v) { *(float4*)p = v; }
 __device__ __forceinline__ void store_out4(uint16_t* p, float4 v) {
-  *(uint2*)p = make_uint2((uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
-                          (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
+  *(uint2*)p = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
 template <class OutT>

@@ -27,7 +27,7 @@ __device__ __forceinline__ uint32_t probe_pair(uint32_t s, bool zero) {
   if (zero) return 0u;
   const uint32_t h = probe_hash(s);
   const float a = (float)(h & 0xffffu) * (1.f / 32768.f) - 1.f, b = (float)(h >> 16) * (1.f / 32768.f) - 1.f;
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  return pack_bf16x2(a, b);
 }
 
 // out[thread] = sum of the thread's accumulators (keeps the MFMAs live);
