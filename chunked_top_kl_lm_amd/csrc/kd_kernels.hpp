@@ -41,9 +41,9 @@ __device__ __forceinline__ void clamp_padding_rows(f32x16 (&acc)[FM][FN], int ro
 // Forward pass of a chunk: per (vocabulary strip of one wave, row t) the
 // running max and sum of exp2 -- the partial logsumexp that the online merge
 // folds into the row's full-vocabulary normaliser.  The logits themselves are
-// never written (the chunk is "folded into the running loss and discarded":
-// Glonce, "Multiverse Computing cuts LLM distillation VRAM by 15x with
-// chunked KL loss", paragraph on Multiverse's two-part fix).
+// never written: each chunk contributes its reductions to the loss and is
+// then dropped (Glonce, "Multiverse Computing cuts LLM distillation VRAM by
+// 15x with chunked KL loss", paragraph on Multiverse's two-part fix).
 //
 // The same epilogue also picks out the logits at the teacher's cached ids:
 // every (t, k) of the chunk is filed beforehand (hit_build_kernel) under the wave
@@ -409,11 +409,30 @@ struct EpiStoreSplit {
 // Head gradient: grad_W[v][j] (+)= tile, accumulated across chunks in fp32
 // (the first chunk stores).  grad_W (2.3 GB at V = 201088, d = 2880) is
 // streamed once per launch, so its loads and stores are non-temporal.
+//
+// A wave reaches its 64 rows of grad_W through a buffer resource that ends
+// at row M, with 32-bit offsets: rows past M read zeros and are not written,
+// and a lane whose column is past N gets an offset beyond any resource, so
+// the update needs neither predicates nor 64-bit address arithmetic per
+// element (the host limits d to 2^20, so a wave's 64 rows span under 2^28
+// bytes and no offset wraps).
 struct EpiAccum {
   float* out;
   int64_t ld;
   int M, N;
   int first;
+
+  static constexpr uint32_t kOutside = 0x80000000u;   // offset beyond every resource
+  static constexpr int kNT = 2;                       // non-temporal cache policy
+
+  // (m0 is the same on every lane of a wave; readfirstlane says so to the
+  // compiler, which keeps the resource in scalar registers)
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(int m0, int nrows) const {
+    const int m0u = __builtin_amdgcn_readfirstlane(m0);
+    const int rows = max(0, min(nrows, M - m0u));
+    const int bytes = __builtin_amdgcn_readfirstlane(rows * (int)ld * 4);
+    return make_rsrc(out + (int64_t)m0u * ld, (uint32_t)bytes);
+  }
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
@@ -421,59 +440,36 @@ struct EpiAccum {
       apply_wide(acc, c);
       return;
     }
-    const bool full = c.m0 + FM * 32 <= M && c.n0 + FN * 32 <= N;
-    if (full) {
-      // old values first (one burst of loads), then the stores
-      if (!first) {
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(c.m0, FM * 32);
+    const uint32_t ld4 = (uint32_t)ld * 4u;
+    // lane offset of column n in the lane's first row (acc_row(0, lane))
+    uint32_t vo[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const float* p = out + (int64_t)(c.m0 + 32 * i) * ld + c.n0 + 32 * j + acc_col(c.lane);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              acc[i][j][r] += __builtin_nontemporal_load(p + (int64_t)acc_row(r, c.lane) * ld);
-          }
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          float* p = out + (int64_t)(c.m0 + 32 * i) * ld + c.n0 + 32 * j + acc_col(c.lane);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __builtin_nontemporal_store(acc[i][j][r], p + (int64_t)acc_row(r, c.lane) * ld);
-        }
-      return;
+    for (int j = 0; j < FN; ++j) {
+      const int n = c.n0 + 32 * j + acc_col(c.lane);
+      vo[j] = n < N ? (uint32_t)(4 * (c.lane >> 5)) * ld4 + (uint32_t)n * 4u : kOutside;
     }
-    // ragged edge: the old values are loaded unconditionally from clamped
-    // (in-bounds) addresses, so the loads stay in flight together; only the
-    // stores are predicated
+    // old values first (one burst of loads), then the stores
     if (!first) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int nc = min(c.n0 + 32 * j + acc_col(c.lane), N - 1);
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int mc = min(c.m0 + 32 * i + acc_row(r, c.lane), M - 1);
-            acc[i][j][r] += __builtin_nontemporal_load(out + (int64_t)mc * ld + nc);
-          }
-        }
+          for (int r = 0; r < 16; ++r)
+            acc[i][j][r] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rs, vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT));
     }
+    // (__float_as_uint takes the element by value; hipcc's __builtin_bit_cast
+    // of a vector-element lvalue reads element 0 instead)
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = c.n0 + 32 * j + acc_col(c.lane);
-        if (n >= N) continue;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = c.m0 + 32 * i + acc_row(r, c.lane);
-          if (m < M) __builtin_nontemporal_store(acc[i][j][r], out + (int64_t)m * ld + n);
-        }
-      }
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs,
+                                                vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT);
   }
 
   // 64 x 160 wave tiles (256 x 320 blocks, 18 KB of the freed LDS ring per
@@ -482,7 +478,6 @@ struct EpiAccum {
   // wave's tile go through LDS and are updated with 16-byte accesses, while
   // columns 0..95 are updated straight from the accumulators.  Requires N
   // and ld multiples of 4 and a 16-byte aligned `out` (checked by the host).
-  // Rows >= M and columns >= N: loads from clamped addresses, no stores.
   static constexpr int kWideStride = 72;   // floats per staged row: 288 B, so the
                                            // two half-waves (rows 4 apart) hit
                                            // disjoint banks
@@ -495,51 +490,48 @@ struct EpiAccum {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           st[(32 * i + acc_row(r, c.lane)) * kWideStride + 32 * (j - 3) + acc_col(c.lane)] = acc[i][j][r];
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(c.m0, 64);
+    const uint32_t ld4 = (uint32_t)ld * 4u;
     // columns 0..95 from the accumulators: all old values in flight, then the stores
+    uint32_t vo[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int n = c.n0 + 32 * j + acc_col(c.lane);
+      vo[j] = n < N ? (uint32_t)(4 * (c.lane >> 5)) * ld4 + (uint32_t)n * 4u : kOutside;
+    }
     if (!first) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          const int nc = min(c.n0 + 32 * j + acc_col(c.lane), N - 1);
+        for (int j = 0; j < 3; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int mc = min(c.m0 + 32 * i + acc_row(r, c.lane), M - 1);
-            acc[i][j][r] += __builtin_nontemporal_load(out + (int64_t)mc * ld + nc);
-          }
-        }
+          for (int r = 0; r < 16; ++r)
+            acc[i][j][r] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rs, vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int n = c.n0 + 32 * j + acc_col(c.lane);
+      for (int j = 0; j < 3; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = c.m0 + 32 * i + acc_row(r, c.lane);
-          if (m < M && n < N) __builtin_nontemporal_store(acc[i][j][r], out + (int64_t)m * ld + n);
-        }
-      }
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs,
+                                                vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT);
     // columns 96..159 from LDS: lane -> row 4q + lane/16, columns 4 (lane % 16) .. +3
     __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the wave's staging writes are done
     f32x4 v[16];
     const int col = 4 * (c.lane & 15);
     const int n = c.n0 + 96 + col;
-    const int nc = min(n, N - 4);
+    const uint32_t vs = n < N ? (uint32_t)(c.lane >> 4) * ld4 + (uint32_t)n * 4u : kOutside;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int row = 4 * q + (c.lane >> 4);
-      v[q] = *(const f32x4*)(st + row * kWideStride + col);
-      if (!first) {
-        const int mc = min(c.m0 + row, M - 1);
-        v[q] += __builtin_nontemporal_load((const f32x4*)(out + (int64_t)mc * ld + nc));
-      }
+      v[q] = *(const f32x4*)(st + (4 * q + (c.lane >> 4)) * kWideStride + col);
+      if (!first)
+        v[q] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vs + (uint32_t)(4 * q) * ld4, 0, kNT));
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = c.m0 + 4 * q + (c.lane >> 4);
-      if (m < M && n < N) __builtin_nontemporal_store(v[q], (f32x4*)(out + (int64_t)m * ld + n));
-    }
+    for (int q = 0; q < 16; ++q)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[q]), rs, vs + (uint32_t)(4 * q) * ld4, 0, kNT);
   }
 };
 
