@@ -5,9 +5,9 @@
 // Per call:
 //   prep            N = #counted positions; clear the loss accumulator
 //   transpose W     W^T (zero-padded) for the hidden-gradient GEMM
-//   for each chunk of `chunk` rows (the pages' method: project one sequence
-//   chunk at a time, fold it into the running loss, discard it, recompute it
-//   in the backward pass -- Glonce, "Multiverse Computing cuts LLM
+//   for each chunk of `chunk` rows (the method: only one chunk's logits
+//   exist at any time; they are reduced into the loss, dropped, and formed
+//   again for the gradient -- Glonce, "Multiverse Computing cuts LLM
 //   distillation VRAM by 15x with chunked KL loss", paragraph on Multiverse's
 //   two-part fix):
 //     transpose H_c   H_c^T for the head-gradient GEMM; teacher-id hit lists

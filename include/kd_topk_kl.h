@@ -3,9 +3,9 @@
  * AMD Instinct MI355X (gfx950).
  *
  * The operation.  A student's hidden states are projected through its output
- * head one sequence chunk at a time; each chunk's full-vocabulary logits are
- * folded into the running loss and discarded, and the backward pass
- * recomputes each chunk instead of storing the sequence x vocabulary grid
+ * head one sequence chunk at a time; a chunk's full-vocabulary logits are
+ * reduced into the loss and then dropped, and the gradient pass forms them
+ * again rather than keeping a sequence x vocabulary grid
  * (Glonce, "Multiverse Computing cuts LLM distillation VRAM by 15x with
  * chunked KL loss", paragraph on Multiverse's two-part fix).  The teacher is
  * represented by an offline cache of its K largest logits per position
