@@ -13,8 +13,8 @@ and verify the rest:
 Cases: the 32-row-block threshold path, the collect-everything path (fewer
 blocks than K), fp32 inputs, padded d, ragged chunks, exact ties (duplicated
 head rows), fully tied rows (the exact fallback), K = V, K = 4096 (the
-maximum, both paths), the full-size head at reduced T, and the cache feeding
-the loss.
+maximum, both paths), the full-size head at reduced T, the cache feeding
+the loss, and 30 seeded random shapes.
 """
 import numpy as np
 import pytest
@@ -183,3 +183,30 @@ def test_timed_build_matches_untimed():
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert all(ev[2 * i].elapsed_time(ev[2 * i + 1]) >= 0 for i in range(nslots))
+
+
+def _sweep_cases(n=30, seed=31):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(1, 400))
+        d = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 600)), int(rng.integers(600, 3000))]))
+        K = int(rng.integers(1, 257))
+        V = int(rng.integers(K, 12000))
+        chunk = int(rng.integers(1, T + 64))
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        out.append((T, d, V, K, chunk, dtype, i))
+    return out
+
+
+@pytest.mark.parametrize("T,d,V,K,chunk,dtype,i", _sweep_cases())
+def test_random_shapes(T, d, V, K, chunk, dtype, i):
+    """Seeded random shapes: ragged chunks and vocabularies, padded d, both
+    paths (a 32-row block per candidate bound, or every logit when the
+    vocabulary has fewer blocks than K), both input dtypes."""
+    rng = np.random.default_rng(700 + i)
+    H = rng.standard_normal((T, d)).astype(np.float32)
+    W = (rng.standard_normal((V, d)) / np.sqrt(d)).astype(np.float32) * 2
+    if dtype == "bf16":
+        H, W = _bf16(H), _bf16(W)
+    _check(H, W, K, chunk, dtype, f"sweep {i}")
