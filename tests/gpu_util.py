@@ -32,9 +32,9 @@ def to_device(x: dict):
         h = _host_tensor(np.asarray(x["hidden"]))
         w = _host_tensor(np.asarray(x["W"]))
     return dict(hidden=h.to(dev), W=w.to(dev),
-                teacher_idx=torch.from_numpy(x["teacher_idx"]).to(dev),
-                teacher_logit=torch.from_numpy(x["teacher_logit"]).to(dev),
-                mask=None if x["mask"] is None else torch.from_numpy(x["mask"]).to(dev))
+                teacher_idx=_host_tensor(x["teacher_idx"]).to(dev),
+                teacher_logit=_host_tensor(x["teacher_logit"]).to(dev),
+                mask=None if x["mask"] is None else _host_tensor(x["mask"]).to(dev))
 
 
 def run_gpu(x: dict, chunk: int | None = None, tau: float | None = None, row_stats=True, status=False):

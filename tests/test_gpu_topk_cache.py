@@ -32,9 +32,10 @@ def _bf16(a):
 
 def _dev(a, dtype):
     import torch
+    from tests.gpu_util import _host_tensor
     if dtype == "bf16":
-        return torch.from_numpy(np.asarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+        return _host_tensor(np.asarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return _host_tensor(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
 
 
 def _run(H, W, K, chunk, dtype):
