@@ -10,7 +10,8 @@ recomputes each chunk's logits from the saved per-row logsumexp.  Checked:
     round-to-nearest-even of the fp32 results), skipping either gradient,
     invalid ids reported by the backward;
   - torch.autograd end to end, with and without an fp32 grad_W accumulator,
-    against the oracle.
+    against the oracle;
+  - 16 seeded random shapes through the split calls.
 """
 import numpy as np
 import pytest
@@ -179,3 +180,47 @@ def test_timed_split_calls_match_untimed():
     assert float(loss_a.item()) == float(loss_b.item()) and torch.equal(rl_a, rl_b)
     assert torch.equal(gH_a, gH_b) and torch.equal(gW_a, gW_b)
     assert all(eb[2 * i].elapsed_time(eb[2 * i + 1]) >= 0 for i in range(nslots))
+
+
+def _split_cases(n=16, seed=53):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(1, 600))
+        d = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 700)), int(rng.integers(700, 3000))]))
+        K = int(rng.integers(1, 129))
+        V = int(rng.integers(K, 8000))
+        chunk = int(rng.integers(1, T + 64))
+        tau = float(np.round(rng.uniform(0.3, 3.0), 2))
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        out.append((T, d, V, K, chunk, tau, dtype, i))
+    return out
+
+
+@pytest.mark.parametrize("T,d,V,K,chunk,tau,dtype,i", _split_cases())
+def test_split_random_shapes(T, d, V, K, chunk, tau, dtype, i):
+    """Seeded random shapes through the split calls: the forward equals the
+    fused call bit for bit, the backward (its own hit lists and teacher
+    probabilities) matches the fused gradients and the oracle."""
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    from tests.gpu_util import run_gpu
+    from tests.test_gpu_parity import _small
+    x = _small(T, d, V, K, dtype, seed=900 + i, tau=tau, masked=tuple(range(0, T, 6)) if T > 3 else (),
+               dup_row=(T // 2 if K >= 2 else None))
+    log(f"[gpu-split] sweep {i}: T={T} d={d} V={V} K={K} chunk={chunk} tau={tau} {dtype}")
+    fused = run_gpu(x, chunk=chunk)
+    t = to_device(x)
+    args = (t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"])
+    loss_s, rl_s, rk_s = kd.fwd(*args, tau=tau, chunk=chunk, row_kl=True)
+    gH_s, gW_s, _ = kd.bwd(*args, rl_s, tau=tau, chunk=chunk)
+    torch.cuda.synchronize()
+    assert float(loss_s.item()) == fused["loss"]
+    assert np.array_equal(rl_s.cpu().numpy(), fused["row_lse"]) and np.array_equal(rk_s.cpu().numpy(), fused["row_kl"])
+    gH, gW = gH_s.float().cpu().numpy(), gW_s.float().cpu().numpy()
+    tight = dtype == "f32"
+    assert rel_f(gH, fused["grad_hidden"]) < (1e-5 if tight else 1e-3)
+    assert rel_f(gW, fused["grad_W"]) < (1e-5 if tight else 1e-3)
+    ref = fused_kl(x["hidden"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], tau)
+    assert rel_f(gH, ref["grad_hidden"]) <= (1e-4 if tight else GRAD_TOL)
+    assert rel_f(gW, ref["grad_W"]) <= (1e-4 if tight else GRAD_TOL)
