@@ -12,7 +12,8 @@ Prints ONE JSON line.  Extra keys: roofline (dominant kernel, live HIP-event
 timing inside the timed region), cpu_baseline (the fp64 oracle on a bounded
 sample of the same workload, host cores), mfma_ceiling (an MFMA-only loop on
 random operands timed after the step: what the MFMA pipes deliver at the
-clock the chip sustains), phases_ms, peak_gib; with --library-gemm also
+clock the chip sustains), phases_ms, gemm_traffic (fabric bytes and GB/s of
+every GEMM phase from the committed counter summary), peak_gib; with --library-gemm also
 library_gemm (torch.matmul on the same contraction shapes, a calibration).
 """
 from __future__ import annotations
@@ -431,6 +432,16 @@ def main() -> int:
     alg_flops = 2.0 * d * V * T / launches
     achieved = alg_flops / (launch_ms * 1e-3) / 1e12
     traffic, traffic_detail = (None, None) if args.split else load_traffic(dom, workload_key(args.workload, T, chunk))
+    # fabric traffic of every GEMM phase (the counter summary's bytes per
+    # launch over this run's launch time), where the summary matches
+    gemm_traffic = {}
+    if not args.split:
+        ndw = -(-nchunks // kd.dw_chunks(T, d, V, K, chunk, dt))
+        for ph in GEMM_PHASES:
+            b, _ = load_traffic(ph, workload_key(args.workload, T, chunk))
+            if b is not None:
+                lms = phase_ms[ph] / (ndw if ph == "gemm_dW" else nchunks)
+                gemm_traffic[ph] = {"bytes_per_launch": b, "launch_ms": lms, "GBps": b / (lms * 1e-3) / 1e9}
 
     if args.copy_probe:
         src = torch.empty(2**30 // 2, dtype=torch.float32, device=dev).fill_(1.0)
@@ -469,6 +480,7 @@ def main() -> int:
             "tflops": ceiling, "what": "MFMA-only loop, random bf16 register operands, no memory traffic",
             "frac_dominant": achieved / ceiling, "frac_step": tflops / ceiling},
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "gemm_traffic": gemm_traffic or None,
         "wall_s_timed": wall,
         "input_gen_s": t_gen,
         "kernel_source_hash": kernel_source_hash(),
