@@ -179,3 +179,29 @@ def test_q_part_of_grad_w():
     e = rel_f(g["grad_W"][10000:], ref["grad_W"][10000:])
     log(f"[gpu] q-part block relF {e:.2e}")
     assert e <= GRAD_TOL
+
+
+def test_timed_call_matches_untimed():
+    """The measured entry point (kd_topk_kl_fwd_bwd_timed, what bench.py
+    times) computes bit for bit what the plain call computes, and every phase
+    interval it records is a valid, non-negative time."""
+    import torch
+    import chunked_top_kl_lm_amd as kd
+    from tests.gpu_util import to_device
+    x = make_inputs(config_for(3, T=700, d=576, V=7000), seed=8)
+    t = to_device(x)
+    args = (t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"])
+    chunk = 256
+    nchunks = -(-700 // chunk)
+    log(f"[gpu] timed vs untimed: T=700 chunk={chunk}")
+    a = kd.fwd_bwd(*args, tau=x["tau"], chunk=chunk, row_stats=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * (kd.KD_NUM_PHASES * nchunks + 2))]
+    for e in evs:
+        e.record()
+    b = kd.fwd_bwd(*args, tau=x["tau"], chunk=chunk, row_stats=True, events=evs)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    times = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(evs) // 2)]
+    assert all(ms >= 0 for ms in times)
+    assert sum(times) > 0
