@@ -107,9 +107,22 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _events(events):
-    """ctypes array of the hipEvent_t handles of already-recorded torch.cuda.Event objects."""
+def _nchunks(T: int, chunk: int) -> int:
+    c = min(int(chunk), int(T))
+    return -(-int(T) // c) if c > 0 else 0
+
+
+def _events(events, needed: int):
+    """ctypes array of the hipEvent_t handles of already-recorded
+    torch.cuda.Event objects; the library records into exactly `needed` of
+    them, so any other count is refused before the call."""
+    if len(events) != needed:
+        raise ValueError(f"events: expected {needed} recorded torch.cuda.Event objects, got {len(events)}")
     return (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+
+
+def _loss_events(events, T: int, chunk: int):
+    return _events(events, 2 * (KD_NUM_PHASES * _nchunks(T, chunk) + 2))
 
 
 def _check_device(dev, **tensors):
@@ -206,7 +219,7 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     if events is None:
         rc = L.kd_topk_kl_fwd_bwd(*args)
     else:
-        rc = L.kd_topk_kl_fwd_bwd_timed(*args, _events(events))
+        rc = L.kd_topk_kl_fwd_bwd_timed(*args, _loss_events(events, T, chunk))
     if rc != 0:
         raise KdError(rc)
     if row_stats:
@@ -266,7 +279,7 @@ def topk_cache(hidden, W, K: int = 100, chunk: int = 2048, workspace=None, event
     if events is None:
         rc = lib().kd_topk_cache_build(*args)
     else:
-        rc = lib().kd_topk_cache_build_timed(*args, _events(events))
+        rc = lib().kd_topk_cache_build_timed(*args, _events(events, 2 * (KD_CACHE_PHASES * _nchunks(T, chunk) + 1)))
     if rc != 0:
         raise KdError(rc)
     return idx, logit
@@ -297,7 +310,7 @@ def fwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0, chun
     if events is None:
         rc = lib().kd_topk_kl_fwd(*args)
     else:
-        rc = lib().kd_topk_kl_fwd_timed(*args, _events(events))
+        rc = lib().kd_topk_kl_fwd_timed(*args, _loss_events(events, T, chunk))
     if rc != 0:
         raise KdError(rc)
     return (loss, rl, rk) if row_kl else (loss, rl)
@@ -350,7 +363,7 @@ def bwd(hidden, W, teacher_idx, teacher_logit, mask, row_lse, tau: float = 1.0, 
     if events is None:
         rc = lib().kd_topk_kl_bwd(*args)
     else:
-        rc = lib().kd_topk_kl_bwd_timed(*args, _events(events))
+        rc = lib().kd_topk_kl_bwd_timed(*args, _loss_events(events, T, chunk))
     if rc != 0:
         raise KdError(rc)
     return gH, gW, gWb

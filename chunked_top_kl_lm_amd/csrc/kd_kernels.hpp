@@ -215,7 +215,11 @@ struct EpiGrad {
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
-    // G values in fp32, in place: acc <- sc * q (sc = g tau m_t / N)
+    // G values in fp32, in place: acc <- sc * q (sc = g tau m_t / N), formed
+    // as one exp2 per element with |sc| folded into the exponent,
+    // q |sc| = exp2(z c2 - (lse2 - log2 |sc|)), and the sign of g applied
+    // after (it is the same for the whole call).  sc = 0 (masked rows, rows
+    // past the chunk, N = 0, g = 0) gives an exponent of -inf, hence 0.
     const int N = (int)c.pf[4];
     const float s = N > 0 ? __builtin_bit_cast(float, c.pf[5]) * (tau / (float)N) : 0.f;
     float sc[FN];
@@ -225,10 +229,19 @@ struct EpiGrad {
       const bool row = c.n0 + 32 * j + acc_col(c.lane) < R;
       sc[j] = row && c.pf[8 + j] ? s : 0.f;
       const float l2 = row ? __builtin_bit_cast(float, c.pf[6 + j]) * lse_to2 : 0.f;
+      const float off = l2 - __log2f(fabsf(sc[j]));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = sc[j] * fast_exp2(fminf(acc[i][j][r] * c2 - l2, 0.f));
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fast_exp2(acc[i][j][r] * c2 - off);
+    }
+    if (s < 0.f) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = -acc[i][j][r];
     }
     if (hit_off) sparse_part<FM, FN>(acc, sc, c);
     if constexpr (E::kBytes == 2 && FM == 4 && FN == 2) {
@@ -240,9 +253,11 @@ struct EpiGrad {
     store_direct<FM, FN>(acc, c);
   }
 
-  // -sc_t p_k at (v = idx[t,k], t) for every (t, k) filed under this wave
-  // tile (duplicate ids each subtract their own p, so P sums them); the
-  // lane that holds the element applies it, so G is rounded once.
+  // -sc_t P at (v = idx[t,k], t) for every (t, k) filed under this wave
+  // tile, where psel holds P once per (t, v) (repeated ids are merged by
+  // merged_target_row, their later entries hold 0, so the order of the list
+  // does not reach the result); the lane that holds the element applies it,
+  // so G is rounded once.
   template <int FM, int FN>
   __device__ __forceinline__ void sparse_part(f32x16 (&acc)[FM][FN], const float (&sc)[FN], const EpiCtx& c) const {
     static_assert(FM * 32 == kHitV && FN * 32 == kHitT, "hit lists are filed by wave tile");
@@ -280,11 +295,9 @@ struct EpiGrad {
   }
 
   // Rows past the vocabulary (z = 0 from zero-filled A rows) get finite junk
-  // in both store paths: the head-gradient GEMM never reads G^T rows >= V,
-  // and the hidden-gradient GEMM multiplies G's columns >= V by the zero
-  // columns of the padded W^T.  Capping the exponent at 0 keeps them finite
-  // (for real rows x*c2 <= lse2 holds up to the rounding of the normaliser,
-  // since both passes produce the same z and the merged sum is >= 1).
+  // in both store paths (|sc| 2^-lse2): the head-gradient GEMM never reads
+  // G^T rows >= V, and the hidden-gradient GEMM multiplies G's columns >= V
+  // by the zero columns of the padded W^T.
   template <int FM, int FN>
   __device__ __forceinline__ void store_direct(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
 #pragma unroll
@@ -579,6 +592,72 @@ __device__ __forceinline__ float teacher_row(const float* logit_row, int K, floa
   return mx + logf(sm);
 }
 
+// The sparse teacher target of one row for the recompute epilogue, with
+// repeated ids merged: P[t, v] = sum of p_k over the k with idx[t, k] = v.
+// The (id, k) pairs are sorted in LDS (bitonic, Kp keys, Kp a power of two
+// >= K); the first k of each id receives P, summed over that id's entries in
+// increasing k, and its later entries receive 0.  The epilogue subtracts
+// every (t, k) entry of its hit lists, so each (t, v) loses exactly one
+// nonzero term whatever order the lists hold, and the gradient is the same
+// bit for bit from call to call.  With distinct ids psel[k] = p_k.  Ids
+// outside [0, V) sort last and get no value (they have no hit-list entry).
+__device__ __forceinline__ uint32_t key_k(unsigned long long key) { return (uint32_t)key; }
+__device__ __forceinline__ uint32_t key_id(unsigned long long key) { return (uint32_t)(key >> 32); }
+
+template <int NT>
+__device__ __forceinline__ void merged_target_row(const int32_t* idx_row, int K, int Kp, int V, const float* s_a,
+                                                  float lse_a, unsigned long long* s_key, float* psel_row) {
+  constexpr unsigned long long kNone = ~0ull;
+  for (int k = threadIdx.x; k < Kp; k += NT) {
+    unsigned long long key = kNone;
+    if (k < K) {
+      const int id = idx_row[k];
+      if (id >= 0 && id < V) key = ((unsigned long long)(uint32_t)id << 32) | (uint32_t)k;
+    }
+    s_key[k] = key;
+  }
+  __syncthreads();
+  for (int size = 2; size <= Kp; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < Kp / 2; i += NT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const unsigned long long a = s_key[lo], b = s_key[hi];
+        if ((a > b) == up) {
+          s_key[lo] = b;
+          s_key[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < K; i += NT) {
+    const unsigned long long key = s_key[i];
+    if (key == kNone) continue;
+    const uint32_t id = key_id(key);
+    if (i > 0 && key_id(s_key[i - 1]) == id) {
+      psel_row[key_k(key)] = 0.f;
+      continue;
+    }
+    float P = 0.f;
+    for (int j = i; j < K && s_key[j] != kNone && key_id(s_key[j]) == id; ++j)
+      P += expf(s_a[key_k(s_key[j])] - lse_a);
+    psel_row[key_k(key)] = P;
+  }
+  __syncthreads();
+}
+
+// LDS of kl_rows_kernel and teacher_p_kernel: Kp sort keys, then K teacher
+// logits / tau.
+__host__ __device__ constexpr int teacher_sort_len(int K) {
+  int p = 1;
+  while (p < K) p <<= 1;
+  return p;
+}
+__host__ __device__ constexpr size_t teacher_lds_bytes(int K) {
+  return (size_t)teacher_sort_len(K) * 8 + (size_t)K * 4;
+}
+
 // ---------------------------------------------------------------------------
 // Small kernels
 // ---------------------------------------------------------------------------
@@ -788,7 +867,10 @@ __global__ __launch_bounds__(256) void kl_rows_kernel(const float2* part2, int l
                                                       float* row_lse, const float* zsel, const int32_t* idx,
                                                       const float* logit, int K, int V, float tau, double* rowkl,
                                                       float* row_kl, float* psel, int32_t* status) {
-  __shared__ float s_a[kMaxK];
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];   // teacher_lds_bytes(K)
+  const int Kp = teacher_sort_len(K);
+  unsigned long long* s_key = (unsigned long long*)s_dyn;
+  float* s_a = (float*)(s_dyn + (size_t)Kp * 8);
   __shared__ float s_red[256];
   __shared__ double s_d[256];
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -819,10 +901,11 @@ __global__ __launch_bounds__(256) void kl_rows_kernel(const float2* part2, int l
     const float z = zsel[(int64_t)t * K + k];
     const float logp = s_a[k] - lse_a;
     const float p = expf(logp);
-    if (psel) psel[(int64_t)t * K + k] = p;   // the recompute epilogue's sparse part
     if (p > 0.f) kl += (double)p * ((double)logp - ((double)z * inv_tau - (double)lse));
   }
   kl = block_reduce<256>(kl, s_d, OpAddD());
+  // the recompute epilogue's sparse part, repeated ids merged
+  if (psel) merged_target_row<256>(idx + (int64_t)t * K, K, Kp, V, s_a, lse_a, s_key, psel + (int64_t)t * K);
   if (tid == 0) {
     rowkl[t] = kl;
     if (row_kl) row_kl[t] = (float)kl;
@@ -840,24 +923,25 @@ __global__ __launch_bounds__(256) void chunk_loss_kernel(const double* rowkl, co
   if (threadIdx.x == 0) *loss_acc += s;
 }
 
-// Teacher probabilities p_k of the chunk's rows for the recompute epilogue's
-// sparse part, in the backward-only call (the fused call gets them from
-// kl_rows_kernel).  One block per chunk row; invalid ids set *status and are
-// left out of the hit lists, so they contribute nothing.
+// The sparse teacher target of the chunk's rows for the recompute epilogue,
+// in the backward-only call (the fused call gets it from kl_rows_kernel):
+// p_k with repeated ids merged (merged_target_row).  One block per chunk row;
+// invalid ids set *status and are left out of the hit lists, so they
+// contribute nothing.  Dynamic LDS: teacher_lds_bytes(K).
 __global__ __launch_bounds__(128) void teacher_p_kernel(const int32_t* idx, const float* logit, int K, int V,
                                                         float tau, float* psel, int32_t* status) {
-  __shared__ float s_a[kMaxK];
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  const int Kp = teacher_sort_len(K);
+  unsigned long long* s_key = (unsigned long long*)s_dyn;
+  float* s_a = (float*)(s_dyn + (size_t)Kp * 8);
   __shared__ float s_red[128];
   const int t = blockIdx.x;
   const float lse_a = teacher_row<128>(logit + (int64_t)t * K, K, 1.f / tau, s_a, s_red);
   for (int k = threadIdx.x; k < K; k += 128) {
     const int id = idx[(int64_t)t * K + k];
-    if (id < 0 || id >= V) {
-      if (status) *status = 7;                // KD_ERR_BAD_INDEX
-      continue;
-    }
-    psel[(int64_t)t * K + k] = expf(s_a[k] - lse_a);
+    if ((id < 0 || id >= V) && status) *status = 7;   // KD_ERR_BAD_INDEX
   }
+  merged_target_row<128>(idx + (int64_t)t * K, K, Kp, V, s_a, lse_a, s_key, psel + (int64_t)t * K);
 }
 
 // grad_hidden rows of the chunk: fixed-order sum of the split-K partials,

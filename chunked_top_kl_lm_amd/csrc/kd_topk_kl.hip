@@ -20,8 +20,8 @@
 //   (the backward-only entry point first recomputes the teacher's P)
 //     GEMM dH         split-K over the vocabulary, fixed-order reduction
 //     GEMM dW         grad_W (+)= G^T H in fp32, once per group of
-//                     consecutive chunks spanning >= 4096 rows (their G^T
-//                     and H^T sit side by side in the workspace)
+//                     consecutive chunks spanning up to 8192 rows (their
+//                     G^T and H^T sit side by side in the workspace)
 //   finalize        loss = tau^2 * acc / N
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -63,10 +63,12 @@ constexpr int kWaveM = TileMain::BM / TileMain::WM;   // vocabulary strip of one
 constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
 // The head-gradient GEMM contracts over at least this many rows per launch
 // (several consecutive chunks when the chunk is smaller): each launch reads
-// and writes the whole fp32 grad_W once, so fewer, longer launches halve
-// that traffic at 2048-row chunks (2.19 vs 2.44 ms per 2048 rows at
-// d = 2880, V = 201088) for one more chunk-sized G^T buffer.
-constexpr int64_t kDwRows = 4096;
+// and writes the whole fp32 grad_W once, so fewer, longer launches cut that
+// traffic.  At 2048-row chunks (d = 2880, V = 201088) 4096 rows per launch
+// took 2.19 vs 2.44 ms per 2048 rows for one chunk, and 8192 rows take 2 ms
+// less per 32K step again (measured against 4096 in the same run), for two
+// more chunk-sized G^T buffers (1.65 GB, independent of T).
+constexpr int64_t kDwRows = 8192;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -353,7 +355,8 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
       hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)cdiv(R, 32), (unsigned)P.ng), dim3(256), 0, st,
                          (const float2*)part, (int)P.R_p, (int)P.nvt, R, part2);
       KD_LAUNCH_CHECK();
-      hipLaunchKernelGGL(kl_rows_kernel, dim3(R), dim3(256), 0, st, (const float2*)part2, (int)P.R_p, (int)P.ng,
+      hipLaunchKernelGGL(kl_rows_kernel, dim3(R), dim3(256), teacher_lds_bytes((int)K), st, (const float2*)part2,
+                         (int)P.R_p, (int)P.ng,
                          lse2, A.row_lse ? A.row_lse + c0 : nullptr, (const float*)zsel, idx_c, logit_c, (int)K,
                          (int)V, tau, rowkl, A.row_kl ? A.row_kl + c0 : nullptr, psel, A.status);
       KD_LAUNCH_CHECK();
@@ -372,8 +375,8 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
     // would have left (phase 4, recorded ahead of phase 3)
     mark(slot + 4, 0);
     if (!P.fwd) {
-      hipLaunchKernelGGL(teacher_p_kernel, dim3(R), dim3(128), 0, st, idx_c, logit_c, (int)K, (int)V, tau, psel,
-                         A.status);
+      hipLaunchKernelGGL(teacher_p_kernel, dim3(R), dim3(128), teacher_lds_bytes((int)K), st, idx_c, logit_c,
+                         (int)K, (int)V, tau, psel, A.status);
       KD_LAUNCH_CHECK();
     }
     mark(slot + 4, 1);

@@ -46,7 +46,7 @@ import functools
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "make_inputs", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "config_for"]
+           "bf16_bits_to_f32", "config_for", "to_device"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -216,3 +216,30 @@ def make_inputs(cfg: Config | int, seed: int = 0, topk_backend: str = "numpy",
                 teacher_logit=np.ascontiguousarray(logit), mask=mask,
                 tau=float(cfg.tau), chunk=int(cfg.chunk), dtype=cfg.dtype,
                 cfg=cfg)
+
+
+def _host_tensor(a: np.ndarray):
+    """A torch view of a host array that is only read (copied to the device):
+    read-only arrays (cached inputs) are wrapped without a host copy."""
+    import warnings
+    import torch
+    with warnings.catch_warnings():
+        warnings.filterwarnings("ignore", message="The given NumPy array is not writable")
+        return torch.from_numpy(a)
+
+
+def to_device(x: dict, device: str = "cuda:0") -> dict:
+    """Copy one workload's arrays to the GPU as torch tensors (bf16 bit
+    patterns become torch.bfloat16 without conversion); plumbing only."""
+    import torch
+    dev = torch.device(device)
+    if x["dtype"] == "bf16":
+        h = _host_tensor(np.asarray(x["hidden"]).view(np.int16)).view(torch.bfloat16)
+        w = _host_tensor(np.asarray(x["W"]).view(np.int16)).view(torch.bfloat16)
+    else:
+        h = _host_tensor(np.asarray(x["hidden"]))
+        w = _host_tensor(np.asarray(x["W"]))
+    return dict(hidden=h.to(dev), W=w.to(dev),
+                teacher_idx=_host_tensor(x["teacher_idx"]).to(dev),
+                teacher_logit=_host_tensor(x["teacher_logit"]).to(dev),
+                mask=None if x["mask"] is None else _host_tensor(x["mask"]).to(dev))

@@ -84,10 +84,11 @@ size_t kd_topk_kl_workspace_bytes(int64_t T, int64_t d, int64_t V, int64_t K,
  * Number of consecutive chunks whose gradient one launch of the
  * head-gradient GEMM (grad_W += G^T H) contracts, for these sizes; 0 if the
  * arguments are invalid.  Each launch reads and writes the whole fp32
- * grad_W once, so a launch takes consecutive chunks until it spans at least
- * 4096 rows (the chunk counted rounded up to a multiple of 256), and never
- * more chunks than there are: max(1, min(nchunks, 4096 / chunk_256)).  The
- * same grouping applies to kd_topk_kl_bwd.  It changes neither the results'
+ * grad_W once, so a launch takes as many consecutive chunks as fit in 8192
+ * rows (the chunk counted rounded up to a multiple of 256), at least one and
+ * never more than there are: max(1, min(nchunks, 8192 / chunk_256)).  The
+ * workspace holds the transposed gradient of that many chunks.  The same
+ * grouping applies to kd_topk_kl_bwd.  It changes neither the results'
  * meaning nor the summation's determinism (fp32 sums in a fixed order).
  */
 int32_t kd_topk_kl_dw_chunks(int64_t T, int64_t d, int64_t V, int64_t K,

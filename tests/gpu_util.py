@@ -6,35 +6,12 @@ import sys
 
 import numpy as np
 
+from datagen import to_device  # noqa: F401  (re-exported for the tests)
+
 
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
-
-
-def _host_tensor(a: np.ndarray):
-    """A torch view of a host array that is only read (copied to the device):
-    read-only arrays (cached inputs) are wrapped without a host copy."""
-    import warnings
-    import torch
-    with warnings.catch_warnings():
-        warnings.filterwarnings("ignore", message="The given NumPy array is not writable")
-        return torch.from_numpy(a)
-
-
-def to_device(x: dict):
-    import torch
-    dev = torch.device("cuda:0")
-    if x["dtype"] == "bf16":
-        h = _host_tensor(np.asarray(x["hidden"]).view(np.int16)).view(torch.bfloat16)
-        w = _host_tensor(np.asarray(x["W"]).view(np.int16)).view(torch.bfloat16)
-    else:
-        h = _host_tensor(np.asarray(x["hidden"]))
-        w = _host_tensor(np.asarray(x["W"]))
-    return dict(hidden=h.to(dev), W=w.to(dev),
-                teacher_idx=_host_tensor(x["teacher_idx"]).to(dev),
-                teacher_logit=_host_tensor(x["teacher_logit"]).to(dev),
-                mask=None if x["mask"] is None else _host_tensor(x["mask"]).to(dev))
 
 
 def run_gpu(x: dict, chunk: int | None = None, tau: float | None = None, row_stats=True, status=False):
@@ -76,3 +53,19 @@ def rel(a: float, b: float) -> float:
 # carries ~2e-3 relative error, an order of magnitude inside 2e-2.
 LOSS_TOL = 1e-3
 GRAD_TOL = 2e-2
+
+# Per-row statistics (returned through row_lse / row_kl): |LSE_gpu - LSE| <=
+# ROW_LSE_TOL nats and |KL_gpu - KL| <= ROW_KL_TOL * max(1, |KL|).  Each is a
+# logsumexp of, or a difference between, logits carrying the fp32 summation
+# error above (~1e-6 relative, measured |dLSE| <= 2e-6 at d = 2880); the bar
+# is the loss bar applied row by row, so a wrong row cannot hide in the mean.
+ROW_LSE_TOL = 1e-3
+ROW_KL_TOL = 1e-3
+
+
+def row_errors(g_lse, g_kl, r_lse, r_kl):
+    """(max |dLSE|, max |dKL| / max(1, |KL|)) over the rows given."""
+    e_lse = float(np.max(np.abs(np.asarray(g_lse, np.float64) - r_lse))) if len(r_lse) else 0.0
+    e_kl = float(np.max(np.abs(np.asarray(g_kl, np.float64) - r_kl) / np.maximum(1.0, np.abs(r_kl)))) \
+        if len(r_kl) else 0.0
+    return e_lse, e_kl

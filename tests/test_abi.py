@@ -58,26 +58,27 @@ def test_workspace_bytes_validation_and_scaling():
     assert a == b > 0
     # chunk larger than T is T
     assert wb(100, 64, 1000, 10, 5000, 0) == wb(100, 64, 1000, 10, 100, 0)
-    # O(chunk*V + V*d): past 4096 rows (one chunk per head-gradient launch)
+    # O(chunk*V + V*d): past 8192 rows (one chunk per head-gradient launch)
     # doubling the chunk grows both gradient layouts, 2 * chunk * V * 2 bytes
-    c1 = wb(65536, 2880, 201088, 100, 4096, 0)
-    c2 = wb(65536, 2880, 201088, 100, 8192, 0)
-    assert 0.9 < (c2 - c1) / (2 * 4096 * 201216 * 2) < 1.3
-    # below it the transposed layout spans 4096 rows of grouped chunks, so
+    c1 = wb(65536, 2880, 201088, 100, 8192, 0)
+    c2 = wb(65536, 2880, 201088, 100, 16384, 0)
+    assert 0.9 < (c2 - c1) / (2 * 8192 * 201216 * 2) < 1.3
+    # below it the transposed layout spans 8192 rows of grouped chunks, so
     # halving the chunk shrinks only the row-major one
-    c0 = wb(65536, 2880, 201088, 100, 2048, 0)
-    assert 0.9 < (c1 - c0) / (2048 * 201216 * 2) < 1.3
+    c0 = wb(65536, 2880, 201088, 100, 4096, 0)
+    assert 0.9 < (c1 - c0) / (4096 * 201216 * 2) < 1.3
     # fp32 path is larger
     assert wb(512, 256, 4096, 16, 128, 1) > wb(512, 256, 4096, 16, 128, 0)
 
 
 def test_dw_chunks_grouping():
     dc = kd.dw_chunks
-    assert dc(32768, 2880, 201088, 100, 2048, 0) == 2
-    assert dc(32768, 2880, 201088, 100, 4096, 0) == 1
+    assert dc(32768, 2880, 201088, 100, 2048, 0) == 4
+    assert dc(32768, 2880, 201088, 100, 4096, 0) == 2
     assert dc(32768, 2880, 201088, 100, 8192, 0) == 1
-    assert dc(32768, 64, 1000, 10, 1000, 1) == 4        # 1000 rows count as 1024
-    assert dc(32768, 64, 1000, 10, 100, 0) == 16        # 100 rows count as 256
+    assert dc(32768, 2880, 201088, 100, 16384, 0) == 1  # at least one
+    assert dc(32768, 64, 1000, 10, 1000, 1) == 8        # 1000 rows count as 1024
+    assert dc(32768, 64, 1000, 10, 100, 0) == 32        # 100 rows count as 256
     assert dc(3000, 64, 1000, 10, 1024, 0) == 3         # never more chunks than there are
     assert dc(100, 64, 1000, 10, 5000, 0) == 1
     assert dc(0, 64, 1000, 10, 100, 0) == 0             # invalid sizes

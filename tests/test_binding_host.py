@@ -39,3 +39,19 @@ def test_workspace_and_status_types():
     with pytest.raises(ValueError, match="status"):
         kd._check_workspace(None, torch.zeros(1, dtype=torch.int64))
     kd._check_workspace(torch.zeros(16, dtype=torch.uint8), torch.zeros(1, dtype=torch.int32))
+
+
+def test_event_count_is_checked_before_the_call():
+    """The timed entry points record into 2 * (phases * nchunks + extra)
+    caller events; a shorter list would make the library read past it."""
+    class Ev:
+        cuda_event = 0
+    assert kd._nchunks(10, 4) == 3 and kd._nchunks(10, 64) == 1 and kd._nchunks(4096, 1024) == 4
+    with pytest.raises(ValueError, match="expected 52"):
+        kd._loss_events([Ev()] * 51, 10, 4)
+    with pytest.raises(ValueError, match="expected 52"):
+        kd._loss_events([Ev()] * 53, 10, 4)
+    assert len(kd._loss_events([Ev()] * 52, 10, 4)) == 52
+    need = 2 * (kd.KD_CACHE_PHASES * 3 + 1)
+    with pytest.raises(ValueError, match=f"expected {need}"):
+        kd._events([Ev()] * (need - 1), need)

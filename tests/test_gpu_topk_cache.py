@@ -32,7 +32,7 @@ def _bf16(a):
 
 def _dev(a, dtype):
     import torch
-    from tests.gpu_util import _host_tensor
+    from datagen import _host_tensor
     if dtype == "bf16":
         return _host_tensor(np.asarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
     return _host_tensor(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")

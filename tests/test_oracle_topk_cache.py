@@ -75,3 +75,85 @@ def test_bf16_bits_are_widened_exactly():
     W = np.array([[0xC000], [0x3F80]], dtype=np.uint16)   # -2.0, 1.0
     idx, val = topk_cache(H, W, 2)
     assert idx.tolist() == [[1, 0]] and val.tolist() == [[1.5, -3.0]]
+
+
+# ---------------------------------------------------------------------------
+# teacher_logits: the fp64 logits the cache builder's GPU checks compare to.
+# Pinned by an exact brute force (math.fsum over exactly widened inputs, the
+# bf16 widening written out here with struct, independent of the oracle's
+# own conversion), for fp32 and bf16-bit inputs and the `rows` selection;
+# planted mistakes (a transposed product, bf16 bits read as integers, rows
+# ignored) must fail it.
+# ---------------------------------------------------------------------------
+import importlib
+import struct
+
+from oracle import teacher_logits
+
+otc = importlib.import_module("oracle.topk_cache")   # the module (the package re-exports a function of that name)
+
+
+def _widen_bf16(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def _brute_logits(H, W, rows, bf16: bool):
+    conv = _widen_bf16 if bf16 else float
+    out = []
+    for t in rows:
+        h = [conv(v) for v in H[t]]
+        out.append([math.fsum(h[j] * conv(W[v][j]) for j in range(len(h))) for v in range(len(W))])
+    return np.array(out)
+
+
+def _pin_teacher_logits():
+    rng = np.random.default_rng(17)
+    T, d, V = 5, 7, 13
+    Hf = rng.standard_normal((T, d)).astype(np.float32)
+    Wf = rng.standard_normal((V, d)).astype(np.float32)
+    z = teacher_logits(Hf, Wf)
+    want = _brute_logits(Hf, Wf, range(T), bf16=False)
+    assert z.shape == (T, V) and z.dtype == np.float64
+    assert np.allclose(z, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    # bf16 bit patterns: every product of two bf16 values is exact in fp64
+    Hb = (Hf.view(np.uint32) >> 16).astype(np.uint16)
+    Wb = (Wf.view(np.uint32) >> 16).astype(np.uint16)
+    zb = teacher_logits(Hb, Wb)
+    wantb = _brute_logits(Hb, Wb, range(T), bf16=True)
+    assert zb.shape == (T, V)
+    assert np.allclose(zb, wantb, rtol=0, atol=1e-12 * np.abs(wantb).max())
+    # rows: in the given order, repeats allowed
+    rows = [3, 0, 3, 4]
+    zr = teacher_logits(Hb, Wb, rows=rows)
+    assert zr.shape == (len(rows), V)
+    assert np.allclose(zr, wantb[rows], rtol=0, atol=1e-12 * np.abs(wantb).max())
+
+
+def test_teacher_logits_exact_brute_force():
+    _pin_teacher_logits()
+
+
+def _transposed(hidden, W, rows=None):
+    Hd = otc.as_f64(hidden)
+    if rows is not None:
+        Hd = Hd[np.asarray(rows)]
+    return (Hd @ otc.as_f64(W).T).T
+
+
+def _no_widening(x, is_bf16_bits=None):
+    return np.asarray(x).astype(np.float64)        # bf16 bits read as integers
+
+
+def _rows_ignored(hidden, W, rows=None):
+    return otc.as_f64(hidden) @ otc.as_f64(W).T
+
+
+@pytest.mark.parametrize("attr,fn", [("teacher_logits", _transposed), ("as_f64", _no_widening),
+                                     ("teacher_logits", _rows_ignored)])
+def test_teacher_logits_pin_catches_planted_mistakes(attr, fn, monkeypatch):
+    import tests.test_oracle_topk_cache as me
+    monkeypatch.setattr(otc, attr, fn)
+    if attr == "teacher_logits":
+        monkeypatch.setattr(me, "teacher_logits", fn)
+    with pytest.raises(AssertionError):
+        _pin_teacher_logits()
