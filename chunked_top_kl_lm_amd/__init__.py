@@ -13,6 +13,7 @@ import os
 __all__ = ["KD_BF16", "KD_F32", "KD_NUM_PHASES", "PHASES", "KD_CACHE_PHASES", "CACHE_PHASES", "KdError", "lib", "workspace_bytes", "fwd_bwd",
            "fwd", "bwd", "fwd_workspace_bytes", "bwd_workspace_bytes", "dw_chunks", "KdTopKKLFunction",
            "kd_topk_kl_loss", "topk_cache", "mfma_probe", "topk_cache_workspace_bytes",
+           "fwd_bwd_noalloc", "NOALLOC_SCRATCH_BYTES",
            "status_str", "STATUS"]
 
 KD_BF16 = 0
@@ -24,7 +25,8 @@ PHASES = ("chunk_prep", "gemm_fwd_lse", "kl_rows", "gemm_bwd_grad", "teacher_p",
           "gemm_dhidden", "dhidden_reduce", "gemm_dW")
 STATUS = {0: "KD_OK", 1: "KD_ERR_NULL_ARG", 2: "KD_ERR_BAD_SHAPE", 3: "KD_ERR_BAD_TAU",
           4: "KD_ERR_BAD_CHUNK", 5: "KD_ERR_DTYPE", 6: "KD_ERR_WORKSPACE",
-          7: "KD_ERR_BAD_INDEX", 8: "KD_ERR_HIP"}
+          7: "KD_ERR_BAD_INDEX", 8: "KD_ERR_HIP", 9: "KD_ERR_NOALLOC_SIZE"}
+NOALLOC_SCRATCH_BYTES = 256 << 20     # KD_NOALLOC_SCRATCH_BYTES
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdtopk.so")
 _lib = None
@@ -50,6 +52,9 @@ def lib() -> ctypes.CDLL:
         L.kd_topk_kl_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, i64,
                                          vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.kd_topk_kl_fwd_bwd.restype = i32
+        L.kd_topk_kl_fwd_bwd_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, f32, i64,
+                                                 vp, vp, vp, vp, vp, vp, vp]
+        L.kd_topk_kl_fwd_bwd_noalloc.restype = i32
         L.kd_topk_kl_fwd_bwd_timed.argtypes = L.kd_topk_kl_fwd_bwd.argtypes + [vp]
         L.kd_topk_kl_fwd_bwd_timed.restype = i32
         L.kd_topk_kl_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
@@ -225,6 +230,40 @@ def fwd_bwd(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
     if row_stats:
         return loss, gH, gW, rl, rk
     return loss, gH, gW
+
+
+def fwd_bwd_noalloc(hidden, W, teacher_idx, teacher_logit, mask=None, tau: float = 1.0,
+                    chunk: int = 2048, out=None, row_stats: bool = False, status=None):
+    """fwd_bwd through kd_topk_kl_fwd_bwd_noalloc: the library allocates
+    nothing and uses its fixed device scratch (NOALLOC_SCRATCH_BYTES per
+    GPU) as the workspace.  `out` = (loss, grad_hidden, grad_W[, row_lse,
+    row_kl]) preallocated by the caller (allocated here if None, which a
+    caller that cannot allocate does not do).  Calls that overlap on one GPU
+    race on the scratch."""
+    import torch
+    L = lib()
+    T, d, V, K, dt = _check_inputs(hidden, W, teacher_idx, teacher_logit, mask)
+    dev = hidden.device
+    if out is None:
+        out = (torch.empty((), dtype=torch.float32, device=dev), torch.empty((T, d), dtype=torch.float32, device=dev),
+               torch.empty((V, d), dtype=torch.float32, device=dev))
+        if row_stats:
+            out = out + (torch.empty(T, dtype=torch.float32, device=dev), torch.empty(T, dtype=torch.float32, device=dev))
+    loss, gH, gW = out[:3]
+    rl, rk = (out[3], out[4]) if row_stats else (None, None)
+    for name, t, shape in (("loss", loss, ()), ("grad_hidden", gH, (T, d)), ("grad_W", gW, (V, d)),
+                           ("row_lse", rl, (T,)), ("row_kl", rk, (T,))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise ValueError(f"out: {name} must be a contiguous float32 tensor of shape {shape}")
+    _check_device(dev, loss=loss, grad_hidden=gH, grad_W=gW, row_lse=rl, row_kl=rk, status=status)
+    _check_workspace(None, status)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = L.kd_topk_kl_fwd_bwd_noalloc(_ptr(hidden), _ptr(W), dt, _ptr(teacher_idx), _ptr(teacher_logit),
+                                      _ptr(mask), T, d, V, K, float(tau), int(chunk), _ptr(loss), _ptr(gH),
+                                      _ptr(gW), _ptr(rl), _ptr(rk), _ptr(status), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KdError(rc)
+    return (loss, gH, gW, rl, rk) if row_stats else (loss, gH, gW)
 
 
 def mfma_probe(out, blocks: int, iters: int, zero_operands: bool = False) -> None:

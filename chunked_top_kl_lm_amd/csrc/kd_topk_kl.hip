@@ -28,6 +28,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kd_topk_kl.h"
 #include "kd_cache.hpp"
 #include "kd_kernels.hpp"
@@ -100,7 +102,10 @@ struct Plan {
   size_t total;
 };
 
-int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t dt, int mode, Plan* p) {
+// lean: one chunk per head-gradient launch (the smallest workspace; used by
+// the allocation-free entry point, whose workspace is a fixed static array).
+int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t dt, int mode, Plan* p,
+                  bool lean = false) {
   if (dt != KD_BF16 && dt != KD_F32) return KD_ERR_DTYPE;
   if (T < 1 || d < 1 || V < 1 || K < 1 || K > V || K > KD_MAX_K) return KD_ERR_BAD_SHAPE;
   if (chunk < 1) return KD_ERR_BAD_CHUNK;
@@ -121,7 +126,7 @@ int32_t make_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int
   P.dw_wide = d % 4 == 0 && round_up(d, TileDhWide::BN) <= round_up(d, P.dw_bn);
   P.Nd_p = round_up(d, P.dh_bn);
   P.nvt = P.V_p / kWaveM;
-  P.dw_group = P.bwd ? (int)std::max<int64_t>(1, std::min<int64_t>(P.nchunks, kDwRows / P.R_p)) : 1;
+  P.dw_group = P.bwd && !lean ? (int)std::max<int64_t>(1, std::min<int64_t>(P.nchunks, kDwRows / P.R_p)) : 1;
   P.R_g = P.dw_group * P.R_p;
   P.nbt = P.R_p / kHitT;
   P.ng = cdiv(P.nvt, kMergeStrips);
@@ -477,15 +482,55 @@ int32_t run(const Plan& P, const Args& A, char* ws) {
 }
 
 int32_t dispatch(int mode, int32_t in_dtype, int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk,
-                 void* workspace, size_t workspace_bytes, const Args& A) {
+                 void* workspace, size_t workspace_bytes, const Args& A, bool lean = false) {
   if (!(A.tau > 0.f) || !isfinite(A.tau)) return KD_ERR_BAD_TAU;
   Plan p;
-  const int32_t st = make_plan(T, d, V, K, chunk, in_dtype, mode, &p);
+  const int32_t st = make_plan(T, d, V, K, chunk, in_dtype, mode, &p, lean);
   if (st != KD_OK) return st;
   if ((((uintptr_t)A.hidden) | ((uintptr_t)A.W)) & 15) return KD_ERR_BAD_SHAPE;
+  if (lean && p.total > workspace_bytes) return KD_ERR_NOALLOC_SIZE;
   if (!workspace || workspace_bytes < p.total || (((uintptr_t)workspace) & 255)) return KD_ERR_WORKSPACE;
   if (in_dtype == KD_BF16) return run<Bf16>(p, A, (char*)workspace);
   return run<F32>(p, A, (char*)workspace);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch of the allocation-free entry point: a file-scope
+// device array that each GPU the library runs on holds from the library's
+// first use on it until the process ends.  Host code never passes the
+// array's name to a kernel or a copy (on the host it names a stand-in, not
+// device memory): the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device that `stream` belongs to (the
+// current device for the null stream).
+int32_t scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return KD_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return KD_ERR_HIP;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return KD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return KD_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return KD_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KD_OK;
 }
 
 size_t workspace_for(int mode, int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int32_t in_dtype) {
@@ -673,6 +718,27 @@ int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype, 
                       grad_hidden, grad_W, row_lse, row_kl, workspace, workspace_bytes, status_dev, stream, nullptr);
 }
 
+int32_t kd_topk_kl_fwd_bwd_noalloc(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
+                                   const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
+                                   int64_t K, float tau, int64_t chunk, float* loss, float* grad_hidden,
+                                   float* grad_W, float* row_lse, float* row_kl, int32_t* status_dev,
+                                   void* stream) {
+  if (!hidden || !W || !teacher_idx || !teacher_logit || !loss || !grad_hidden || !grad_W) return KD_ERR_NULL_ARG;
+  kd::Args a{hidden, W, teacher_idx, teacher_logit, mask, tau, loss, row_lse, row_kl, nullptr, grad_hidden, KD_F32,
+             grad_W, 0, nullptr, status_dev, (hipStream_t)stream, nullptr};
+  // argument and size checks come first, so a call that cannot run touches
+  // no device state
+  kd::Plan p;
+  const int32_t st = kd::make_plan(T, d, V, K, chunk, in_dtype, kd::kFused, &p, true);
+  if (st != KD_OK) return st;
+  if (!(tau > 0.f) || !isfinite(tau)) return KD_ERR_BAD_TAU;
+  if (p.total > KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_NOALLOC_SIZE;
+  void* ws = nullptr;
+  const int32_t se = kd::scratch_address((hipStream_t)stream, &ws);
+  if (se != KD_OK) return se;
+  return kd::dispatch(kd::kFused, in_dtype, T, d, V, K, chunk, ws, KD_NOALLOC_SCRATCH_BYTES, a, true);
+}
+
 int32_t kd_topk_kl_fwd_bwd_timed(const void* hidden, const void* W, int32_t in_dtype, const int32_t* teacher_idx,
                                  const float* teacher_logit, const uint8_t* mask, int64_t T, int64_t d, int64_t V,
                                  int64_t K, float tau, int64_t chunk, float* loss, float* grad_hidden, float* grad_W,
@@ -804,6 +870,9 @@ const char* kd_status_str(int32_t s) {
     case KD_ERR_WORKSPACE: return "workspace is NULL, too small or not 256-byte aligned";
     case KD_ERR_BAD_INDEX: return "a teacher id is outside [0, V)";
     case KD_ERR_HIP: return "a HIP launch failed";
+    case KD_ERR_NOALLOC_SIZE:
+      return "the sizes need more workspace than the allocation-free entry point's fixed device scratch "
+             "(KD_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
   }
 }

@@ -60,6 +60,8 @@ extern "C" {
 #define KD_ERR_WORKSPACE 6   /* workspace NULL or smaller than required         */
 #define KD_ERR_BAD_INDEX 7   /* (device) a teacher id is outside [0, V)         */
 #define KD_ERR_HIP 8         /* a HIP launch failed                             */
+#define KD_ERR_NOALLOC_SIZE 9 /* kd_topk_kl_fwd_bwd_noalloc: the sizes need more */
+                             /* than KD_NOALLOC_SCRATCH_BYTES of workspace      */
 
 /* Input element types of `hidden` and `W`. */
 #define KD_BF16 0            /* bfloat16, row-major                             */
@@ -133,6 +135,39 @@ int32_t kd_topk_kl_fwd_bwd(const void* hidden, const void* W, int32_t in_dtype,
                            float* row_lse, float* row_kl,
                            void* workspace, size_t workspace_bytes,
                            int32_t* status_dev, void* stream);
+
+/*
+ * kd_topk_kl_fwd_bwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace and allocates nothing (no hipMalloc,
+ * hipFree or allocating library call): its workspace is a fixed device
+ * array of KD_NOALLOC_SCRATCH_BYTES inside the library, which every GPU the
+ * library runs on holds from the library's first use on that GPU until the
+ * process ends.  The caller still passes inputs and outputs, as for
+ * kd_topk_kl_fwd_bwd (same arguments and meaning, minus the workspace).
+ *
+ * The head gradient is contracted one chunk per launch (the smallest
+ * workspace), so with several chunks grad_W's fp32 sums run in another
+ * fixed order than kd_topk_kl_fwd_bwd's (results agree to rounding; with a
+ * single chunk they are the same bits).  Sizes whose workspace would exceed
+ * KD_NOALLOC_SCRATCH_BYTES return KD_ERR_NOALLOC_SIZE before anything is
+ * enqueued; other errors as for kd_topk_kl_fwd_bwd, and KD_ERR_HIP if the
+ * scratch's device address cannot be obtained.
+ *
+ * All calls on one GPU share that GPU's scratch, which keeps the last call's
+ * contents (none of which a later call relies on): calls that can overlap
+ * on one GPU -- concurrent streams, or threads -- race and must be
+ * serialised by the caller.
+ */
+#define KD_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int32_t kd_topk_kl_fwd_bwd_noalloc(const void* hidden, const void* W, int32_t in_dtype,
+                                   const int32_t* teacher_idx,
+                                   const float* teacher_logit, const uint8_t* mask,
+                                   int64_t T, int64_t d, int64_t V, int64_t K,
+                                   float tau, int64_t chunk,
+                                   float* loss, float* grad_hidden, float* grad_W,
+                                   float* row_lse, float* row_kl,
+                                   int32_t* status_dev, void* stream);
 
 /* Number of timed phases per chunk (see kd_topk_kl_fwd_bwd_timed). */
 #define KD_NUM_PHASES 8

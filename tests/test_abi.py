@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
                                           "kd_topk_kl_dw_chunks", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
                                           "kd_topk_cache_workspace_bytes", "kd_topk_cache_build",
                                           "kd_mfma_probe", "kd_topk_kl_fwd_timed", "kd_topk_kl_bwd_timed",
-                                          "kd_topk_cache_build_timed"}
+                                          "kd_topk_cache_build_timed", "kd_topk_kl_fwd_bwd_noalloc"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         assert kd.status_str(code) and kd.status_str(code) != "unknown status"
     assert kd.status_str(99) == "unknown status"
 
@@ -219,3 +219,27 @@ def test_header_constants_match_the_binding():
                       ("KD_BF16", kd.KD_BF16), ("KD_F32", kd.KD_F32)):
         assert re.search(rf"#define {name} (\d+)", src).group(1) == str(val), name
     assert len(kd.PHASES) == kd.KD_NUM_PHASES and len(kd.CACHE_PHASES) == kd.KD_CACHE_PHASES
+
+
+def _call_noalloc(**kw):
+    L = kd.lib()
+    a = dict(hidden=0x10000, W=0x20000, dt=0, idx=0x30000, logit=0x40000, mask=None, T=64, d=64, V=1000,
+             K=10, tau=1.0, chunk=32, loss=0x50000, gH=0x60000, gW=0x70000, rl=None, rk=None, status=None)
+    a.update(kw)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kd_topk_kl_fwd_bwd_noalloc(v(a["hidden"]), v(a["W"]), a["dt"], v(a["idx"]), v(a["logit"]),
+                                        v(a["mask"]), a["T"], a["d"], a["V"], a["K"], a["tau"], a["chunk"],
+                                        v(a["loss"]), v(a["gH"]), v(a["gW"]), v(a["rl"]), v(a["rk"]),
+                                        v(a["status"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=None), 1), (dict(gW=None), 1), (dict(tau=0.0), 3), (dict(K=0), 2), (dict(chunk=0), 4),
+    (dict(dt=3), 5),
+    # the 32K workload's head needs ~2.8 GB of workspace even with one chunk
+    # per head-gradient launch: refused before any device call
+    (dict(T=32768, d=2880, V=201088, K=100, chunk=2048), 9),
+    (dict(T=64, d=4096, V=100000, K=100, chunk=64), 9),
+])
+def test_noalloc_host_errors(kw, code):
+    assert _call_noalloc(**kw) == code
