@@ -42,7 +42,6 @@ __device__ __forceinline__ uint64_t cand_key(float z, uint32_t id) {
   return ((uint64_t)fkey(z) << 32) | (uint64_t)(0xffffffffu - id);
 }
 
-constexpr int kBlockRows = 32;   // vocabulary rows per block maximum
 
 // Pass 1: per 32-row vocabulary block and column (row t), the largest logit
 // of the block's valid rows, stored per row t: out[t][block].
@@ -220,7 +219,6 @@ __global__ __launch_bounds__(256) void cache_select_kernel(const int* cnt, const
 // products (fp32, summed along d), streamed in batches of kFbBatch ids
 // through a sorted top-K kept in LDS.  Slow (a full pass over W per row);
 // it runs only for rows with more tied candidates than the list holds.
-constexpr int kFbBatch = 1024;
 
 template <class E>
 __global__ __launch_bounds__(256) void cache_fallback_kernel(const typename E::T* H, int64_t ldh,

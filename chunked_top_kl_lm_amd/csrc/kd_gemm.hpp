@@ -30,6 +30,8 @@
 #include <type_traits>
 #include <stdint.h>
 
+#include "kd_layout.hpp"
+
 namespace kd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -170,16 +172,8 @@ struct PrefetchSteps<T, std::void_t<decltype(T::kPrefetchSteps)>> {
 // makes every wave's LDS writes visible; the stage overwritten next is the
 // one all waves finished reading before that same barrier.
 // ---------------------------------------------------------------------------
-// 16-byte slot permutation of an LDS row r of RB bytes (see above): for
-// 64-byte rows f(r) = (r >> 2) & 3, for 128-byte rows f(r) = (r >> 1) & 7
-// (both measured conflict-free for the MFMA fragment reads).
-template <int RB>
-__device__ __forceinline__ int swz(int r) {
-  static_assert(RB == 64 || RB == 128, "row bytes");
-  return RB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
-}
-__device__ __forceinline__ int swz64(int r) { return swz<64>(r); }
-
+// (swz<RB> in kd_layout.hpp is the 16-byte slot permutation of an LDS row
+// of RB bytes; dma_src_offset the source offset it implies.)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -368,13 +362,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
   uint32_t voffA[C::IA], voffB[C::IB];
 #pragma unroll
   for (int i = 0; i < C::IA; ++i) {
-    const int r = C::RPD * (wid + C::NW * i) + lane / UPR;
-    voffA[i] = (uint32_t)(r * strideA + (((lane % UPR) ^ swz<RB>(r)) << 4));
+    voffA[i] = dma_src_offset<RB>(C::RPD * (wid + C::NW * i) + lane / UPR, lane, strideA);
   }
 #pragma unroll
   for (int i = 0; i < C::IB; ++i) {
-    const int r = C::RPD * (wid + C::NW * i) + lane / UPR;
-    voffB[i] = (uint32_t)(r * strideB + (((lane % UPR) ^ swz<RB>(r)) << 4));
+    voffB[i] = dma_src_offset<RB>(C::RPD * (wid + C::NW * i) + lane / UPR, lane, strideB);
   }
 
   f32x16 acc[C::FM][C::FN];
@@ -431,9 +423,5 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_kernel(GemmShape g, Epi 
 
   epi.template apply<C::FM, C::FN>(acc, ctx);
 }
-
-// Row (M) index of register r of lane l inside a 32x32 tile, column index.
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-__device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
 }  // namespace kd

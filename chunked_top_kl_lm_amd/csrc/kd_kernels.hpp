@@ -11,7 +11,6 @@
 
 namespace kd {
 
-constexpr int kMaxK = 4096;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -50,8 +49,6 @@ __device__ __forceinline__ void clamp_padding_rows(f32x16 (&acc)[FM][FN], int ro
 // sub-tile that holds z[t, idx[t,k]], and the wave copies those values from
 // its accumulators to zsel[t*K + k].  The top-K gather of the KL thus reads
 // no W rows.
-constexpr int kHitV = 128;   // vocabulary rows of one forward-GEMM wave tile
-constexpr int kHitT = 64;    // chunk rows of one forward-GEMM wave tile
 
 struct EpiLsePartial {
   float2* part;   // [nvt][ldp]: (max x2, sum exp2(x2 - max)) per strip and row
@@ -98,10 +95,9 @@ struct EpiLsePartial {
         for (int q = 0; q < cnt; ++q) {
           const uint32_t hx = (uint32_t)__builtin_amdgcn_readlane((int)hv.x, q);
           const uint32_t hy = (uint32_t)__builtin_amdgcn_readlane((int)hv.y, q);
-          const int vl = (int)(hy >> 6), tl = (int)(hy & 63);
-          const int rr = vl & 31;
-          const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
-          const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
+          const int vl = hit_code_v(hy), tl = hit_code_t(hy);
+          const int r = acc_reg_of(vl & 31);                   // register and lane holding that element
+          const int owner = acc_lane_of(vl & 31, tl);
           float z = 0.f;
 #pragma unroll
           for (int i = 0; i < FM; ++i)
@@ -279,10 +275,9 @@ struct EpiGrad {
       for (int q = 0; q < cnt; ++q) {
         const uint32_t hy = (uint32_t)__builtin_amdgcn_readlane((int)hv.y, q);
         const float p = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), q));
-        const int vl = (int)(hy >> 6), tl = (int)(hy & 63);
-        const int rr = vl & 31;
-        const int r = 4 * (rr >> 3) + (rr & 3);              // accumulator register (acc_row inverse)
-        const int owner = (tl & 31) + 32 * ((rr >> 2) & 1);  // lane holding that element
+        const int vl = hit_code_v(hy), tl = hit_code_t(hy);
+        const int r = acc_reg_of(vl & 31);                   // register and lane holding that element
+        const int owner = acc_lane_of(vl & 31, tl);
         if (c.lane == owner) {
 #pragma unroll
           for (int i = 0; i < FM; ++i)
@@ -330,7 +325,7 @@ struct EpiGrad {
   //              apart by 256 bytes, spread over the banks);
   //   G^T staging [128 v][64 t], 128-byte rows, 64-byte halves swapped on
   //              rows with bit 2 set (the two half-waves write rows 4 apart).
-  static constexpr int kStageBytes = 16384;
+  static constexpr int kStageBytes = kGradStageBytes;
 
   __device__ __forceinline__ void store_staged(f32x16 (&acc)[4][2], const EpiCtx& c) const {
     char* lds = c.smem + c.wid * (c.smem_bytes / c.nwaves);
@@ -345,15 +340,15 @@ struct EpiGrad {
           const int vl0 = 32 * i + 8 * g4 + 4 * (c.lane >> 5);
           pk[i][j][g4] = make_uint2(pack_bf16x2(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1]),
                                     pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]));
-          *(uint2*)(lds + tl * 256 + (((vl0 >> 3) ^ (tl & 15)) << 4) + ((vl0 & 7) << 1)) = pk[i][j][g4];
+          *(uint2*)(lds + g_stage_offset(tl, vl0)) = pk[i][j][g4];
         }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the wave's staging writes are done
     // G: 64 rows x 16 slots; lane -> row 4q + lane/16, slot lane % 16
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int t = 4 * q + (c.lane >> 4), u = c.lane & 15;
-      const u32x4 val = *(const u32x4*)(lds + t * 256 + ((u ^ (t & 15)) << 4));
+      const int t = g_read_row(q, c.lane), u = g_read_unit(c.lane);
+      const u32x4 val = *(const u32x4*)(lds + g_read_offset(q, c.lane));
       __builtin_nontemporal_store(val, (u32x4*)(G + (int64_t)(c.n0 + t) * ldg + c.m0 + 8 * u));
     }
     // G^T staging (the wave's LDS operations run in order: the reads above
@@ -371,7 +366,7 @@ struct EpiGrad {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int vl = vl0 + e;
-            *(uint16_t*)(lds + vl * 128 + ((tl * 2) ^ (((vl >> 2) & 1) << 6))) = (uint16_t)h[e];
+            *(uint16_t*)(lds + gt_stage_offset(vl, tl)) = (uint16_t)h[e];
           }
         }
     }
@@ -379,8 +374,8 @@ struct EpiGrad {
     // G^T: 128 rows x 8 slots; lane -> row 8q + lane/8, slot lane % 8
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int v = 8 * q + (c.lane >> 3), u = c.lane & 7;
-      const u32x4 val = *(const u32x4*)(lds + v * 128 + ((u * 16) ^ (((v >> 2) & 1) << 6)));
+      const int v = gt_read_row(q, c.lane), u = gt_read_unit(c.lane);
+      const u32x4 val = *(const u32x4*)(lds + gt_read_offset(q, c.lane));
       __builtin_nontemporal_store(val, (u32x4*)(Gt + (int64_t)(c.m0 + v) * ldgt + c.n0 + 8 * u));
     }
   }
@@ -435,14 +430,13 @@ struct EpiAccum {
   int M, N;
   int first;
 
-  static constexpr uint32_t kOutside = 0x80000000u;   // offset beyond every resource
   static constexpr int kNT = 2;                       // non-temporal cache policy
 
   // (m0 is the same on every lane of a wave; readfirstlane says so to the
   // compiler, which keeps the resource in scalar registers)
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(int m0, int nrows) const {
     const int m0u = __builtin_amdgcn_readfirstlane(m0);
-    const int rows = max(0, min(nrows, M - m0u));
+    const int rows = accum_rows(m0u, nrows, M);
     const int bytes = __builtin_amdgcn_readfirstlane(rows * (int)ld * 4);
     return make_rsrc(out + (int64_t)m0u * ld, (uint32_t)bytes);
   }
@@ -458,10 +452,7 @@ struct EpiAccum {
     // lane offset of column n in the lane's first row (acc_row(0, lane))
     uint32_t vo[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = c.n0 + 32 * j + acc_col(c.lane);
-      vo[j] = n < N ? (uint32_t)(4 * (c.lane >> 5)) * ld4 + (uint32_t)n * 4u : kOutside;
-    }
+    for (int j = 0; j < FN; ++j) vo[j] = accum_lane_offset(c.n0 + 32 * j + acc_col(c.lane), N, c.lane, ld4);
     // old values first (one burst of loads), then the stores
     if (!first) {
 #pragma unroll
@@ -471,7 +462,7 @@ struct EpiAccum {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             acc[i][j][r] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                rs, vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT));
+                rs, accum_elem_offset(vo[j], i, r, ld4), 0, kNT));
     }
     // (__float_as_uint takes the element by value; hipcc's __builtin_bit_cast
     // of a vector-element lvalue reads element 0 instead)
@@ -482,7 +473,7 @@ struct EpiAccum {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs,
-                                                vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT);
+                                                accum_elem_offset(vo[j], i, r, ld4), 0, kNT);
   }
 
   // 64 x 160 wave tiles (256 x 320 blocks, 18 KB of the freed LDS ring per
@@ -491,9 +482,8 @@ struct EpiAccum {
   // wave's tile go through LDS and are updated with 16-byte accesses, while
   // columns 0..95 are updated straight from the accumulators.  Requires N
   // and ld multiples of 4 and a 16-byte aligned `out` (checked by the host).
-  static constexpr int kWideStride = 72;   // floats per staged row: 288 B, so the
-                                           // two half-waves (rows 4 apart) hit
-                                           // disjoint banks
+  // (kWideStride = 72 floats per staged row: 288 B, so the two half-waves,
+  // rows 4 apart, hit disjoint banks)
   __device__ __forceinline__ void apply_wide(f32x16 (&acc)[2][5], const EpiCtx& c) const {
     float* st = (float*)(c.smem + c.wid * (c.smem_bytes / c.nwaves));   // [64][72]
 #pragma unroll
@@ -502,16 +492,13 @@ struct EpiAccum {
       for (int j = 3; j < 5; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          st[(32 * i + acc_row(r, c.lane)) * kWideStride + 32 * (j - 3) + acc_col(c.lane)] = acc[i][j][r];
+          st[wide_stage_index(i, j, r, c.lane)] = acc[i][j][r];
     const __amdgpu_buffer_rsrc_t rs = rows_rsrc(c.m0, 64);
     const uint32_t ld4 = (uint32_t)ld * 4u;
     // columns 0..95 from the accumulators: all old values in flight, then the stores
     uint32_t vo[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int n = c.n0 + 32 * j + acc_col(c.lane);
-      vo[j] = n < N ? (uint32_t)(4 * (c.lane >> 5)) * ld4 + (uint32_t)n * 4u : kOutside;
-    }
+    for (int j = 0; j < 3; ++j) vo[j] = accum_lane_offset(c.n0 + 32 * j + acc_col(c.lane), N, c.lane, ld4);
     if (!first) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -520,7 +507,7 @@ struct EpiAccum {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             acc[i][j][r] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                rs, vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT));
+                rs, accum_elem_offset(vo[j], i, r, ld4), 0, kNT));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -529,22 +516,21 @@ struct EpiAccum {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs,
-                                                vo[j] + (uint32_t)(acc_row(r, 0) + 32 * i) * ld4, 0, kNT);
+                                                accum_elem_offset(vo[j], i, r, ld4), 0, kNT);
     // columns 96..159 from LDS: lane -> row 4q + lane/16, columns 4 (lane % 16) .. +3
     __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the wave's staging writes are done
     f32x4 v[16];
-    const int col = 4 * (c.lane & 15);
-    const int n = c.n0 + 96 + col;
-    const uint32_t vs = n < N ? (uint32_t)(c.lane >> 4) * ld4 + (uint32_t)n * 4u : kOutside;
+    const int col = wide_read_col(c.lane);
+    const uint32_t vs = wide_lane_offset(c.n0 + 96 + col, N, c.lane, ld4);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      v[q] = *(const f32x4*)(st + (4 * q + (c.lane >> 4)) * kWideStride + col);
+      v[q] = *(const f32x4*)(st + wide_read_row(q, c.lane) * kWideStride + col);
       if (!first)
-        v[q] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vs + (uint32_t)(4 * q) * ld4, 0, kNT));
+        v[q] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, wide_elem_offset(vs, q, ld4), 0, kNT));
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[q]), rs, vs + (uint32_t)(4 * q) * ld4, 0, kNT);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[q]), rs, wide_elem_offset(vs, q, ld4), 0, kNT);
   }
 };
 
@@ -647,17 +633,6 @@ __device__ __forceinline__ void merged_target_row(const int32_t* idx_row, int K,
   __syncthreads();
 }
 
-// LDS of kl_rows_kernel and teacher_p_kernel: Kp sort keys, then K teacher
-// logits / tau.
-__host__ __device__ constexpr int teacher_sort_len(int K) {
-  int p = 1;
-  while (p < K) p <<= 1;
-  return p;
-}
-__host__ __device__ constexpr size_t teacher_lds_bytes(int K) {
-  return (size_t)teacher_sort_len(K) * 8 + (size_t)K * 4;
-}
-
 // ---------------------------------------------------------------------------
 // Small kernels
 // ---------------------------------------------------------------------------
@@ -741,7 +716,7 @@ __global__ __launch_bounds__(1024) void hit_build_kernel(const int32_t* idx, int
     if (id < 0 || id >= V) continue;
     const int pos = base + atomicAdd(&s_h[id / kHitV], 1);
     const int t = e / K;                             // row within the group
-    hits[pos] = make_uint2((uint32_t)(base + e), (uint32_t)(((id % kHitV) << 6) | t));
+    hits[pos] = make_uint2((uint32_t)(base + e), hit_code(id, t));
   }
 }
 
@@ -825,7 +800,6 @@ __global__ __launch_bounds__(256) void pad_kernel(const typename E::T* src, int6
 // partials into one.  Block = 32 rows x 8 strip slices; consecutive threads
 // read consecutive rows of one strip (coalesced); fixed merge order.  The
 // second level (over the groups) is done by kl_rows_kernel.
-constexpr int kMergeStrips = 64;
 
 __device__ __forceinline__ void lse_combine(float& M, float& L, float m2, float l2) {
   if (l2 <= 0.f) return;                      // empty: strip with no vocabulary rows
