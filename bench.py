@@ -37,6 +37,7 @@ PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 GEMM_PHASES = ("gemm_fwd_lse", "gemm_bwd_grad", "gemm_dhidden", "gemm_dW")
 KERNEL_SOURCES = ("chunked_top_kl_lm_amd/csrc/kd_gemm.hpp", "chunked_top_kl_lm_amd/csrc/kd_kernels.hpp",
+                  "chunked_top_kl_lm_amd/csrc/kd_layout.hpp", "chunked_top_kl_lm_amd/csrc/kd_plan.hpp",
                   "chunked_top_kl_lm_amd/csrc/kd_topk_kl.hip")
 # epilogue type in each GEMM phase's kernel name (rocprofv3 reports kernel names)
 PHASE_KERNEL_TAGS = {"gemm_fwd_lse": "EpiLsePartial", "gemm_bwd_grad": "EpiGrad",

@@ -594,6 +594,39 @@ template <int NT>
 __device__ __forceinline__ void merged_target_row(const int32_t* idx_row, int K, int Kp, int V, const float* s_a,
                                                   float lse_a, unsigned long long* s_key, float* psel_row) {
   constexpr unsigned long long kNone = ~0ull;
+  // Rows rarely repeat an id: for K <= kDupScanK a pairwise scan (each id
+  // against the ids before it, read four at a time from LDS) decides first,
+  // and a row without repeats takes p_k as it is.  The outcome does not
+  // depend on timing, and either path gives the same P.
+  constexpr int kDupScanK = 512;
+  __shared__ int s_dup;
+  if (K <= kDupScanK) {
+    int* s_id = (int*)s_key;                   // Kp >= K ints fit the key array
+    for (int k = threadIdx.x; k < Kp; k += NT) s_id[k] = k < K ? idx_row[k] : -1;
+    if (threadIdx.x == 0) s_dup = 0;
+    __syncthreads();
+    for (int k = threadIdx.x; k < K; k += NT) {
+      const int id = s_id[k];
+      if (id < 0 || id >= V) continue;
+      bool dup = false;
+      for (int k2 = 0; k2 < (k & ~3) && !dup; k2 += 4) {
+        const int4 w = *(const int4*)(s_id + k2);
+        dup = w.x == id || w.y == id || w.z == id || w.w == id;
+      }
+      for (int k2 = k & ~3; k2 < k && !dup; ++k2) dup = s_id[k2] == id;
+      if (dup) s_dup = 1;
+    }
+    __syncthreads();
+    const bool any = s_dup != 0;
+    __syncthreads();                           // s_id is overwritten below
+    if (!any) {
+      for (int k = threadIdx.x; k < K; k += NT) {
+        const int id = idx_row[k];
+        if (id >= 0 && id < V) psel_row[k] = expf(s_a[k] - lse_a);
+      }
+      return;
+    }
+  }
   for (int k = threadIdx.x; k < Kp; k += NT) {
     unsigned long long key = kNone;
     if (k < K) {
