@@ -206,6 +206,16 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = None) -> int:
     copy_f = max(max(v) for k, v in fetch.items() if "copyBuffer" in k)
     copy_w = max(max(v) for k, v in write.items() if "copyBuffer" in k)
     scale = {"fetch": COPY_PROBE_BYTES / copy_f, "write": COPY_PROBE_BYTES / copy_w}
+    # the streaming-GEMM check (--copy-probe): each cache-builder pass reads
+    # W [V, d] bf16 once; the workload's head is d=2880, V=201088
+    from datagen import config_for
+    hc = config_for(3)
+    w_bytes = 2.0 * hc.V * hc.d
+    stream = {}
+    for tag in ("EpiBlockMax", "EpiCollect"):
+        f = [x for k, v in fetch.items() if tag in k for x in v]
+        if f:
+            stream[tag] = {"raw_fetch_bytes": max(f), "w_bytes": w_bytes, "implied_scale": w_bytes / max(f)}
     kernels = {}
     for phase, tag in PHASE_KERNEL_TAGS.items():
         f = [x for k, v in fetch.items() if tag in k and "kd::" in k for x in v]
@@ -216,6 +226,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = None) -> int:
     from datagen import config_for
     cfg = config_for(3)       # the counter runs use bench.py's default workload
     rec = {"kernel_source_hash": kernel_source_hash(), "workload": workload_key(3, cfg.T, cfg.chunk),
+           "gemm_stream_check": stream,
            "copy_scale": scale,
            "copy_raw_bytes": {"fetch": copy_f, "write": copy_w}, "kernels": kernels}
     with open(out or os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as fh:
@@ -227,6 +238,9 @@ def ingest_pmc(fetch_csv: str, write_csv: str, out: str = None) -> int:
               f"{k['fetch_raw_bytes'] / 1e9:.3f} | {k['write_raw_bytes'] / 1e9:.3f} |")
     print(f"\nCopy calibration (2 GiB copy): FETCH_SIZE read {copy_f / 2**30:.3f} GiB (scale {scale['fetch']:.3f}), "
           f"WRITE_SIZE read {copy_w / 2**30:.3f} GiB (scale {scale['write']:.3f}).")
+    for tag, r in stream.items():
+        print(f"Streaming GEMM check ({tag}, reads W once): FETCH_SIZE read {r['raw_fetch_bytes'] / 1e9:.3f} GB "
+              f"for W's {r['w_bytes'] / 1e9:.3f} GB (implied scale {r['implied_scale']:.3f}).")
     return 0
 
 
@@ -482,6 +496,14 @@ def main() -> int:
         src = torch.empty(2**30 // 2, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        # a GEMM that reads its big operand exactly once: the cache builder
+        # on one 256-row chunk (one column tile), whose two head-GEMM passes
+        # (EpiBlockMax, EpiCollect kernels) each stream W once through the
+        # same LDS-DMA loads as the loss's GEMMs; their FETCH_SIZE against
+        # W's bytes checks that the copy calibration holds for these loads
+        kd.topk_cache(t["hidden"][:256].contiguous(), t["W"], K=K, chunk=256)
         torch.cuda.synchronize()
 
     ceiling = mfma_ceiling(kd, torch, dev) if dt == kd.KD_BF16 else None
