@@ -1,9 +1,11 @@
 """Full-size workloads on the GPU, in the launch configuration bench.py times.
 
 The 8K and 32K workloads are compared with the oracle element by element in
-test_gpu_fullsize_oracle.py.  At T = 131072 / 262144 the oracle would take
-tens of minutes, so these tests check (and, at 32K, check again on the way
-to the split calls):
+test_gpu_fullsize_oracle.py.  At T = 131072 / 262144 the whole oracle would
+take tens of minutes, so these tests compare one chunk's rows in full (the
+first 4096 rows at 128K, the last 4096 at 256K: row logsumexp, row KL and
+grad_hidden element by element) and check (and, at 32K, check again on the
+way to the split calls):
   - sampled rows (first, last, masked, random) of row_lse, row_kl and
     grad_hidden against the oracle's per-row results, element by element;
   - the loss against tau^2 * sum_t m_t KL_t / N recomputed in fp64 from the
@@ -23,7 +25,7 @@ import pytest
 
 from datagen import config_for, make_inputs, to_device
 from oracle import fused_kl_rows
-from tests.gpu_util import GRAD_TOL, LOSS_TOL, log, rel, rel_f
+from tests.gpu_util import GRAD_TOL, LOSS_TOL, ROW_KL_TOL, ROW_LSE_TOL, log, rel, rel_f, row_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -145,15 +147,41 @@ def test_topk_cache_full_size_sampled_rows():
             assert sorted(ids.tolist()) == sorted(ref_idx[i].tolist())
 
 
+def _rows_against_oracle(x, cfg, out, r0, r1, block=1024):
+    """Every row of [r0, r1) against the oracle: row logsumexp, row KL and
+    grad_hidden element by element (the oracle's per-row results take the
+    gradient scale from the whole sequence's mask)."""
+    import torch
+    log(f"[gpu-full] oracle rows [{r0}, {r1}) in full")
+    e_lse = e_kl = 0.0
+    num = den = 0.0
+    for b0 in range(r0, r1, block):
+        rows = np.arange(b0, min(r1, b0 + block))
+        ref = fused_kl_rows(x["hidden"], x["W"], x["teacher_idx"], x["teacher_logit"], x["mask"], cfg.tau, rows)
+        a, k = row_errors(out["row_lse"][rows], out["row_kl"][rows], ref["row_lse"], ref["row_kl"])
+        e_lse, e_kl = max(e_lse, a), max(e_kl, k)
+        g = out["gH"][torch.from_numpy(rows).to("cuda:0")].cpu().numpy().astype(np.float64)
+        num += float(((g - ref["grad_hidden_rows"]) ** 2).sum())
+        den += float((ref["grad_hidden_rows"] ** 2).sum())
+        log(f"[gpu-full]   rows up to {rows[-1] + 1} done")
+    e_gh = (num / den) ** 0.5
+    log(f"[gpu-full] rows [{r0}, {r1}): max|dLSE| {e_lse:.2e}  max rel|dKL| {e_kl:.2e}  dH relF {e_gh:.2e}")
+    assert e_lse <= ROW_LSE_TOL and e_kl <= ROW_KL_TOL and e_gh <= GRAD_TOL
+
+
 def test_long_128k_full_tau2():
     x, cfg, out = _run_full(4)
     _checks(x, cfg, out)
+    # the first chunk (4096 rows, tau = 2, its peaked rows among them) in full
+    _rows_against_oracle(x, cfg, out, 0, cfg.chunk)
 
 
 def test_extreme_256k_full_and_memory_is_t_independent():
     import chunked_top_kl_lm_amd as kd
     x, cfg, out = _run_full(5)
     _checks(x, cfg, out, n_random=4)
+    # the last chunk in full
+    _rows_against_oracle(x, cfg, out, cfg.T - cfg.chunk, cfg.T)
     peak_256k = out["peak"]
     del out, x
     import torch
