@@ -34,14 +34,14 @@ def _run_full(num, T=None):
     import torch
     import chunked_top_kl_lm_amd as kd
     cfg = config_for(num, **({"T": T} if T else {}))
-    log(f"[gpu-full] generating workload {num} T={cfg.T}")
+    log(f"[gpu-full] generating {cfg.name} T={cfg.T}")
     x = make_inputs(cfg, seed=0, topk_backend="torch-cuda")
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
     t = to_device(x)
     st = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    log(f"[gpu-full] workload {num}: T={cfg.T} chunk={cfg.chunk} tau={cfg.tau}")
+    log(f"[gpu-full] {cfg.name}: T={cfg.T} chunk={cfg.chunk} tau={cfg.tau}")
     loss, gH, gW, rl, rk = kd.fwd_bwd(t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"],
                                       tau=cfg.tau, chunk=cfg.chunk, row_stats=True, status=st)
     torch.cuda.synchronize()
@@ -101,7 +101,7 @@ def test_gptoss_32k_full():
     import chunked_top_kl_lm_amd as kd
     t = out["t"]
     args = (t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"], t["mask"])
-    log("[gpu-full] workload 3 through the split calls")
+    log("[gpu-full] gptoss-32k (T=32768) through the split calls")
     loss_s, rl_s = kd.fwd(*args, tau=cfg.tau, chunk=cfg.chunk)
     gH_s, gW_s, _ = kd.bwd(*args, rl_s, tau=cfg.tau, chunk=cfg.chunk)
     torch.cuda.synchronize()

@@ -48,8 +48,9 @@ def test_tiny_fp32_full():
 
 @pytest.mark.parametrize("num,T,chunk", [(2, 600, 256), (3, 520, 256), (4, 300, 4096), (5, 400, 128)])
 def test_workload_full_d_v(num, T, chunk):
-    x = make_inputs(config_for(num, T=T), seed=0)
-    _check(x, f"workload {num} T={T}", chunk=chunk)
+    cfg = config_for(num, T=T)
+    x = make_inputs(cfg, seed=0)
+    _check(x, f"{cfg.name} T={T}", chunk=chunk)
 
 
 @pytest.mark.parametrize("chunk", [1, 37, 128, 1024, 300])

@@ -44,7 +44,7 @@ def test_split_matches_fused_and_oracle(num, T, chunk):
     import torch
     import chunked_top_kl_lm_amd as kd
     x = _inputs(num, T)
-    log(f"[gpu-split] workload {num} T={T} chunk={chunk}")
+    log(f"[gpu-split] {config_for(num).name} T={T} chunk={chunk}")
     t = to_device(x)
     st = torch.full((1,), -1, dtype=torch.int32, device="cuda:0")
     loss_f, gH_f, gW_f, rl_f, rk_f = kd.fwd_bwd(t["hidden"], t["W"], t["teacher_idx"], t["teacher_logit"],
