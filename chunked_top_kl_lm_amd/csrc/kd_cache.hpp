@@ -9,16 +9,21 @@
 // changes remove different bottlenecks").
 //
 // Per chunk of rows, with the same GEMM as the loss:
-//   pass 1  z^T = W H_c^T; the epilogue keeps, per 32-row vocabulary block
-//           and row, the block's largest logit (EpiBlockMax);
+//   GEMM    z^T = W H_c^T; the epilogue keeps, per 32-row vocabulary block
+//           and row, the block's largest logit, and stores the chunk's fp32
+//           logits row by row (EpiBlockMax);
 //   select  per row, the K-th largest of those block maxima: a lower bound
 //           theta_t such that at least K logits are >= theta_t (K of the
 //           blocks have their maximum >= it); radix select on order-
 //           preserving keys (cache_threshold_kernel);
-//   pass 2  the same GEMM again (identical z); the epilogue appends every
-//           z >= theta_t of row t to the row's candidate list (EpiCollect);
+//   collect one streaming pass over the stored logits appends every
+//           z >= theta_t of row t to the row's candidate list
+//           (cache_collect_kernel);
 //   sort    per row, the candidates by (z descending, id ascending), the
 //           first K written out (cache_select_kernel).
+// Keeping the chunk's logits (chunk x V fp32) costs one HBM write and one
+// read of them where a second GEMM pass would cost as much MFMA work as the
+// first.
 // Rows with more candidates than the list holds (many logits tied at or
 // above theta_t) are redone exactly by cache_fallback_kernel, which streams
 // the vocabulary through a sorted top-K in LDS with its own dot products.
@@ -43,21 +48,28 @@ __device__ __forceinline__ uint64_t cand_key(float z, uint32_t id) {
 }
 
 
-// Pass 1: per 32-row vocabulary block and column (row t), the largest logit
-// of the block's valid rows, stored per row t: out[t][block].
+// The GEMM's epilogue: per 32-row vocabulary block and column (row t), the
+// largest logit of the block's valid rows, stored per row t: out[t][block];
+// and the tile's logits, stored as z[t][v] (rows of ldz floats; entries at
+// v >= V hold padding and are never read).  The logits go through the
+// wave's 16 KB of the freed LDS ring, one 32-column half at a time, so that
+// they leave as 16-byte non-temporal stores of whole 512-byte row segments.
 struct EpiBlockMax {
   float* out;   // [rows][ldb]: row t's block maxima contiguous
   int ldb;      // V_p / 32 (a multiple of 8)
   int V;
+  float* z;     // [R_p][ldz] the chunk's logits
+  int64_t ldz;  // V_p
 
   template <int FM, int FN>
   __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
     static_assert(FM == 4, "a wave strip holds four 32-row blocks (one 16-byte store per row)");
     const int rows_valid = V - c.m0;
-    if (rows_valid <= 0) return;                    // no valid block here (never read)
+    if (rows_valid <= 0) return;                    // no valid row here (never read)
     if (rows_valid < FM * 32) clamp_padding_rows<FM, FN>(acc, rows_valid, c.lane);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
+      const int n = c.n0 + 32 * j + acc_col(c.lane);
       float mx[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -66,10 +78,33 @@ struct EpiBlockMax {
         for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
         mx[i] = fmaxf(m, __shfl_xor(m, 32));
       }
-      // lane < 32: column (row t) n0 + 32 j + lane, blocks m0/32 .. +3
-      if (c.lane < 32)
-        *(f32x4*)(out + (int64_t)(c.n0 + 32 * j + c.lane) * ldb + c.m0 / kBlockRows) =
-            f32x4{mx[0], mx[1], mx[2], mx[3]};
+      // lane < 32: column (row t) n, blocks m0/32 .. +3
+      if (c.lane < 32) *(f32x4*)(out + (int64_t)n * ldb + c.m0 / kBlockRows) = f32x4{mx[0], mx[1], mx[2], mx[3]};
+      store_half(acc, j, c);
+    }
+  }
+
+  // columns 32 j .. 32 j + 31 of the wave's tile: staged [32 t][128 v], then
+  // each read of a lane is 4 consecutive v of one row, and 32 lanes store a
+  // row's 512 bytes (the wave's LDS operations run in order, so the second
+  // half's writes follow the first half's reads)
+  template <int FM, int FN>
+  __device__ __forceinline__ void store_half(f32x16 (&acc)[FM][FN], int j, const EpiCtx& c) const {
+    static_assert(FM == 4, "128-row strips");
+    char* lds = c.smem + c.wid * (c.smem_bytes / c.nwaves);
+    const int tl = acc_col(c.lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(f32x4*)(lds + cz_stage_offset(tl, 32 * i + 8 * g4 + 4 * (c.lane >> 5))) =
+            f32x4{acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]};
+    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): the wave's staging writes are done
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const f32x4 val = *(const f32x4*)(lds + cz_read_offset(q, c.lane));
+      __builtin_nontemporal_store(
+          val, (f32x4*)(z + cz_global_offset(c.n0 + 32 * j + cz_read_row(q, c.lane), ldz, c.m0, cz_read_unit(c.lane))));
     }
   }
 };
@@ -133,36 +168,42 @@ __global__ __launch_bounds__(256) void cache_threshold_kernel(const float* bmax,
   if (tid == 0) theta[t] = fkey_inv(prefix);
 }
 
-// Pass 2: every valid z >= theta_t goes to row t's candidate list
-// (cand[t][0, cap), count cnt[t]; appends past cap only count).
-struct EpiCollect {
-  const float* theta;
-  int* cnt;
-  uint2* cand;      // (float bits, id)
-  int cap;
-  int V, R;
-
-  template <int FM, int FN>
-  __device__ __forceinline__ void apply(f32x16 (&acc)[FM][FN], const EpiCtx& c) const {
+// Collect: every valid z >= theta_t of row t of the stored logits goes to
+// the row's candidate list (cand[t][0, cap), count cnt[t]; appends past cap
+// only count).  One block per row streams the row's V floats with 16-byte
+// loads, four per thread in flight.
+__global__ __launch_bounds__(256) void cache_collect_kernel(const float* z, int64_t ldz, int V, const float* theta,
+                                                            int* cnt, uint2* cand, int cap) {
+  __shared__ int s_n;
+  const int t = blockIdx.x;
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  const float th = theta[t];
+  const float* row = z + (int64_t)t * ldz;
+  uint2* out = cand + (int64_t)t * cap;
+  // ldz is a multiple of 256 >= V: every 16-byte load that starts below V
+  // stays inside the row
+  for (int v0 = 4 * (int)threadIdx.x; v0 < V; v0 += 4 * 4 * 256) {
+    f32x4 q[4];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = c.n0 + 32 * j + acc_col(c.lane);
-      if (n >= R) continue;
-      const float th = theta[n];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = c.m0 + 32 * i + acc_row(r, c.lane);
-          const float z = acc[i][j][r];
-          if (v < V && z >= th) {
-            const int pos = atomicAdd(&cnt[n], 1);
-            if (pos < cap) cand[(int64_t)n * cap + pos] = make_uint2(__float_as_uint(z), (uint32_t)v);
-          }
-        }
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * 4 * 256;
+      q[u] = v < V ? __builtin_nontemporal_load((const f32x4*)(row + v)) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = v0 + u * 4 * 256 + e;
+        if (v < V && q[u][e] >= th) {
+          const int pos = atomicAdd(&s_n, 1);
+          if (pos < cap) out[pos] = make_uint2(__float_as_uint(q[u][e]), (uint32_t)v);
+        }
+      }
   }
-};
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[t] = s_n;
+}
 
 // In-LDS bitonic sort of n (a power of two) uint64 keys, descending.
 __device__ __forceinline__ void bitonic_desc(uint64_t* s, int n) {

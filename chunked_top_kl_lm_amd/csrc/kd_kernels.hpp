@@ -684,10 +684,6 @@ __global__ __launch_bounds__(1024) void prep_kernel(const uint8_t* mask, int64_t
   }
 }
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int* p, int64_t n, int v) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
-}
-
 // Teacher-id hit lists of a chunk, filed by forward-GEMM wave tile: one
 // block per 64-row group g of the chunk sorts the group's (t, k) entries by
 // vocabulary strip id / kHitV (counting sort in LDS: count, scan, fill).

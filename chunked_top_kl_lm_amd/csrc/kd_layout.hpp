@@ -126,6 +126,26 @@ KD_HD constexpr int gt_read_offset(int q, int lane) {
 constexpr int kGradStageBytes = 16384;
 
 // ---------------------------------------------------------------------------
+// Cache builder: the GEMM epilogue stores the chunk's logits z[t][v] (rows of
+// ldz floats, ldz a multiple of 256) through 16 KB of LDS per wave, one
+// 32-column half of its 128 x 64 tile at a time, staged as [32 t][128 v]
+// fp32: 512-byte rows, 16-byte unit u of row t at u ^ t.
+// ---------------------------------------------------------------------------
+// byte offset of the 16-byte write of v = vl0 .. vl0 + 3 (vl0 a multiple of 4) of row tl
+KD_HD constexpr int cz_stage_offset(int tl, int vl0) { return tl * 512 + (((vl0 >> 2) ^ tl) << 4); }
+// 16-byte read q of a lane: row cz_read_row, v = 4 * cz_read_unit .. + 3
+KD_HD constexpr int cz_read_row(int q, int lane) { return 2 * q + (lane >> 5); }
+KD_HD constexpr int cz_read_unit(int lane) { return lane & 31; }
+KD_HD constexpr int cz_read_offset(int q, int lane) {
+  return cz_read_row(q, lane) * 512 + ((cz_read_unit(lane) ^ cz_read_row(q, lane)) << 4);
+}
+// element offset in z of that read's four values: row n, columns m0 + 4 unit ..
+KD_HD constexpr int64_t cz_global_offset(int n, int64_t ldz, int m0, int unit) {
+  return (int64_t)n * ldz + m0 + 4 * unit;
+}
+constexpr int kCacheStageBytes = 16384;
+
+// ---------------------------------------------------------------------------
 // Teacher rows: LDS of kl_rows_kernel and teacher_p_kernel (Kp 64-bit sort
 // keys, Kp the power of two >= K, then K floats).
 // ---------------------------------------------------------------------------

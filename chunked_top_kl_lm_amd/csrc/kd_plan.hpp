@@ -179,7 +179,7 @@ struct CachePlan {
   int64_t nb32;       // 32-row vocabulary blocks with a valid row
   int cap;            // candidate list length per row (power of two)
   int half;           // fallback: power of two >= max(K, batch)
-  size_t off_wp, off_hp, off_bmax, off_theta, off_cnt, off_cand, off_ovf, total;
+  size_t off_wp, off_hp, off_bmax, off_theta, off_cnt, off_cand, off_ovf, off_z, total;
 };
 
 inline int pow2ceil(int64_t x) {
@@ -223,6 +223,7 @@ inline int32_t make_cache_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64
   P.off_cnt = o; o = align256(o + (size_t)P.R_p * sizeof(int));
   P.off_cand = o; o = align256(o + (size_t)P.R_p * P.cap * (2 * sizeof(uint32_t)));
   P.off_ovf = o; o = align256(o + (size_t)P.R_p * sizeof(int));
+  P.off_z = o; o = align256(o + (size_t)P.R_p * P.V_p * sizeof(float));                   // [R_p][V_p] logits
   P.total = o;
   return KD_OK;
 }

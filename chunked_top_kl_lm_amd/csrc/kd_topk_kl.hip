@@ -409,6 +409,7 @@ int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t
   int* cnt = (int*)(ws + P.off_cnt);
   uint2* cand = (uint2*)(ws + P.off_cand);
   int* ovf = (int*)(ws + P.off_ovf);
+  float* zc = (float*)(ws + P.off_z);
   const int64_t d = P.d, V = P.V, K = P.K;
 
   const T* Wsrc = (const T*)W;
@@ -441,10 +442,9 @@ int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t
       Hsrc = Hp;
       ldh = P.d_p;
     }
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)cdiv(R, 256)), dim3(256), 0, st, cnt, (int64_t)R, 0);
-    KD_LAUNCH_CHECK();
     GemmShape g = make_shape<TileMain>(Wsrc, ldw, (int)V, Hsrc, ldh, R, kbytes_d, 1, 1);
-    if (launch_gemm<TileMain, E>(g, EpiBlockMax{bmax, (int)(P.V_p / kBlockRows), (int)V}, st) != hipSuccess)
+    if (launch_gemm<TileMain, E>(g, EpiBlockMax{bmax, (int)(P.V_p / kBlockRows), (int)V, zc, P.V_p}, st) !=
+        hipSuccess)
       return KD_ERR_HIP;
     mark(slot + 0, 1);
     mark(slot + 1, 0);
@@ -453,8 +453,9 @@ int32_t run_cache(const CachePlan& P, const void* hidden, const void* W, int32_t
     KD_LAUNCH_CHECK();
     mark(slot + 1, 1);
     mark(slot + 2, 0);
-    if (launch_gemm<TileMain, E>(g, EpiCollect{theta, cnt, cand, P.cap, (int)V, R}, st) != hipSuccess)
-      return KD_ERR_HIP;
+    hipLaunchKernelGGL(cache_collect_kernel, dim3(R), dim3(256), 0, st, (const float*)zc, P.V_p, (int)V,
+                       (const float*)theta, cnt, cand, P.cap);
+    KD_LAUNCH_CHECK();
     mark(slot + 2, 1);
     mark(slot + 3, 0);
     int32_t* oi = out_idx + c0 * K;

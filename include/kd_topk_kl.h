@@ -310,10 +310,11 @@ int32_t kd_topk_kl_bwd_timed(const void* hidden, const void* W, int32_t in_dtype
  *             logits z[t, v] = h_t . W_v, in descending order of z; equal
  *             logits are ordered by the lower id.
  *  out_logit  device [T, K] float32 (written): those logits.
- *  chunk      rows processed at a time (the logits of a chunk are computed
- *             twice and never stored).
+ *  chunk      rows processed at a time (the chunk's logits are computed once,
+ *             kept in the workspace as fp32 and scanned once more for the
+ *             candidates of each row).
  * Workspace: kd_topk_cache_workspace_bytes(...) bytes, 256-byte aligned;
- * O(chunk * (V / 32 + K)), independent of T beyond the chunk.  Host errors
+ * O(chunk * V), independent of T beyond the chunk.  Host errors
  * as for kd_topk_kl_fwd_bwd.  Logits are fp32 sums of exact bf16 (or fp32)
  * products; rows where more than about 2K logits tie at or above the
  * selection threshold are recomputed by a slower exact path with plain dot
@@ -334,10 +335,11 @@ int32_t kd_topk_cache_build(const void* hidden, const void* W, int32_t in_dtype,
  * to 2 * (KD_CACHE_PHASES * nchunks + 1) hipEvent_t created by the caller
  * (nchunks = ceil(T / min(chunk, T))); events[2*i] is recorded before and
  * events[2*i + 1] after
- *   i = c * KD_CACHE_PHASES + p   phase p of chunk c: 0 the first head GEMM
- *       (per-row block maxima, after the chunk's padded copy if any),
- *       1 the threshold selection, 2 the second head GEMM (candidates),
- *       3 the sort of the candidates and the exact fallback;
+ *   i = c * KD_CACHE_PHASES + p   phase p of chunk c: 0 the head GEMM
+ *       (per-row block maxima and the stored logits, after the chunk's
+ *       padded copy if any), 1 the threshold selection, 2 the scan of the
+ *       stored logits for candidates, 3 the sort of the candidates and the
+ *       exact fallback;
  *   i = KD_CACHE_PHASES * nchunks  the prologue (padded copy of W, if any).
  * Everything else is as for kd_topk_cache_build; KD_ERR_NULL_ARG if events
  * is NULL.

@@ -19,6 +19,11 @@
 //     G^T [V_p][R_g];
 //   logsumexp partials and hit-list bounds stay inside their buffers;
 //   operand staging: DMA offsets of valid rows fit the K extent and resource;
+//   cache builder: the logit staging writes each (t, v) once and every read
+//     returns 4 consecutive v of one row; the 16-byte logit stores land on
+//     their own (t, v) inside [R_p][V_p] and cover a wave tile once; the collect
+//     loads stay inside a row; the cache plan's buffers are aligned,
+//     ordered, disjoint and inside the total;
 //   plan: for every mode, buffers are 256-byte aligned, ordered, disjoint,
 //     inside the total, and at least as large as the kernels index them; a
 //     host buffer of exactly `total` bytes is written region by region (the
@@ -305,6 +310,100 @@ static void check_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk
   }
 }
 
+// ---------------------------------------------------------------------------
+// Cache builder: the GEMM epilogue's logit stores and block maxima, the
+// collect kernel's row loads, and the cache plan's buffers.
+// the logit staging of one wave and column half: every (t, v) written once,
+// 16-byte aligned, inside the 16 KB slice, each register at its own (t, v);
+// every read returns 4 consecutive v of one row and the reads cover the half
+static void check_cache_staging() {
+  std::set<int> wr;
+  for (int lane = 0; lane < 64; ++lane)
+    for (int i = 0; i < 4; ++i)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int tl = acc_col(lane), vl0 = 32 * i + 8 * g4 + 4 * (lane >> 5);
+        const int o = cz_stage_offset(tl, vl0);
+        CHECK(o % 16 == 0 && o >= 0 && o + 16 <= kCacheStageBytes, "cache staging write %d", o);
+        for (int e = 0; e < 4; ++e) {
+          CHECK(32 * i + acc_row(4 * g4 + e, lane) == vl0 + e, "cache staging register %d holds v %d",
+                4 * g4 + e, vl0 + e);
+          wr.insert(o + 4 * e);
+        }
+      }
+  CHECK(wr.size() == 32 * 128, "cache staging writes cover %zu of 4096", wr.size());
+  std::set<int> rd;
+  for (int q = 0; q < 16; ++q)
+    for (int lane = 0; lane < 64; ++lane) {
+      const int t = cz_read_row(q, lane), u = cz_read_unit(lane);
+      CHECK(t < 32 && u < 32 && cz_read_offset(q, lane) == cz_stage_offset(t, 4 * u), "cache staging read");
+      rd.insert(t * 32 + u);
+    }
+  CHECK(rd.size() == 32 * 32, "cache staging reads cover %zu of 1024 units", rd.size());
+  // 8 waves' slices fit the logit GEMM's LDS ring
+  CHECK(8 * kCacheStageBytes <= TileMain::STAGES * (TileMain::BM + TileMain::BN) * TileMain::RB, "cache staging LDS");
+}
+
+static std::set<std::pair<int64_t, int64_t>> g_cache_tiles_done;
+
+// the global stores of a wave tile at the first and last strip and column
+// block: 16-byte aligned, each value at its own (t, v) inside [R_p][V_p],
+// the tile covered once (depends on V_p and R_p only; each pair once)
+static void check_cache_tiles(int64_t V, int64_t V_p, int64_t R_p) {
+  if (!g_cache_tiles_done.insert({V_p, R_p}).second) return;
+  const int64_t ldz = planted("cache-z-stride") ? V : V_p;
+  const int m0s[] = {0, (int)(V_p - 128)};
+  const int n0s[] = {0, (int)(R_p - 64)};
+  for (int m0 : m0s)
+    for (int n0 : n0s) {
+      std::set<int64_t> seen;
+      for (int j = 0; j < 2; ++j)
+        for (int q = 0; q < 16; ++q)
+          for (int lane = 0; lane < 64; ++lane) {
+            const int t = n0 + 32 * j + cz_read_row(q, lane), u = cz_read_unit(lane);
+            const int64_t o = cz_global_offset(t, ldz, m0, u);
+            CHECK(o % 4 == 0, "logit store not 16-byte aligned (V_p %lld)", (long long)V_p);
+            for (int e = 0; e < 4; ++e) {
+              const int64_t want = (int64_t)t * V_p + m0 + 4 * u + e;
+              CHECK(o + e == want, "logit store element (t %d, v %d) at %lld, want %lld", t, m0 + 4 * u + e,
+                    (long long)(o + e), (long long)want);
+              CHECK(o + e >= 0 && o + e < R_p * V_p, "logit store past the buffer");
+              seen.insert(o + e);
+            }
+          }
+      CHECK(seen.size() == 128 * 64, "logit stores cover %zu of a wave tile's 8192", seen.size());
+    }
+}
+
+static void check_cache_plan(int64_t T, int64_t d, int64_t V, int64_t K, int64_t chunk, int dt) {
+  CachePlan P;
+  if (make_cache_plan(T, d, V, K, chunk, dt, &P) != KD_OK) return;
+  check_cache_tiles(V, P.V_p, P.R_p);
+  // block maxima: row n, blocks m0/32 .. +3 of V_p/32; collect loads: a
+  // 16-byte load starting at v < V (v a multiple of 4) ends inside the row
+  CHECK((P.V_p / kBlockRows) % 4 == 0 && P.V_p % 256 == 0, "block-maxima rows / logit rows");
+  CHECK(((V - 1) / 4) * 4 + 4 <= P.V_p, "collect load past the row");
+  const size_t eb = (size_t)P.eb;
+  const std::vector<Buf> bufs = {
+      {"W pad", P.off_wp, (size_t)V * P.d_p * eb, P.pad_d},
+      {"H pad", P.off_hp, (size_t)P.R_p * P.d_p * eb, P.pad_d},
+      {"block maxima", P.off_bmax, (size_t)P.R_p * (P.V_p / kBlockRows) * 4, true},
+      {"theta", P.off_theta, (size_t)P.R_p * 4, true},
+      {"counts", P.off_cnt, (size_t)P.R_p * 4, true},
+      {"candidates", P.off_cand, (size_t)P.R_p * P.cap * 8, true},
+      {"overflow", P.off_ovf, (size_t)P.R_p * 4, true},
+      {"logits", P.off_z, (size_t)P.R_p * P.V_p * 4, true},
+  };
+  size_t prev_end = 0;
+  for (const Buf& b : bufs) {
+    if (!b.used) continue;
+    CHECK(b.off % 256 == 0, "cache %s not 256-byte aligned", b.name);
+    CHECK(b.off >= prev_end, "cache %s overlaps the previous buffer", b.name);
+    CHECK(b.off + b.need <= P.total, "cache %s ends past the workspace", b.name);
+    prev_end = b.off + b.need;
+  }
+  CHECK(P.cap >= 2 * K || P.cap == 8192, "candidate list shorter than 2K");
+}
+
 int main(int argc, char** argv) {
   for (int i = 1; i < argc; ++i)
     if (!strcmp(argv[i], "--plant") && i + 1 < argc) g_plant = argv[++i];
@@ -312,6 +411,7 @@ int main(int argc, char** argv) {
   check_acc_layout();
   check_hit_codes();
   check_grad_staging();
+  check_cache_staging();
 
   // head-gradient RMW over ragged shapes, all three tile widths
   const int Vs[] = {1, 5, 127, 128, 255, 257, 3000, 5000, 201088};
@@ -339,6 +439,14 @@ int main(int argc, char** argv) {
                 check_plan(T, d, V, K, c, dt, mode, false);
                 if (mode == kFused) check_plan(T, d, V, K, c, dt, mode, true);
               }
+
+  // cache-builder plans over ragged shapes, both dtypes
+  for (int64_t T : Ts)
+    for (int64_t d : dps)
+      for (int64_t V : Vps)
+        for (int64_t K : Ks)
+          for (int64_t c : chunks)
+            for (int dt = 0; dt < 2; ++dt) check_cache_plan(T, d, V, K, c, dt);
 
   printf("index checks: %ld, failures: %ld%s%s\n", g_checks, g_fail, g_plant.empty() ? "" : ", planted: ",
          g_plant.c_str());

@@ -10,7 +10,8 @@ aligned, disjoint, inside the workspace and as large as the kernels index
 them (see the file's header).  Each planted mistake -- a head-gradient
 resource sized to the padded tile instead of the vocabulary, a lost column
 guard, the gradient staging without its swizzle, one G^T slot for a group
-of chunks, a workspace total that leaves out the last buffer -- must fail.
+of chunks, a workspace total that leaves out the last buffer, the cache
+builder's logit rows at the unpadded vocabulary stride -- must fail.
 """
 import os
 import shutil
@@ -55,6 +56,7 @@ def test_every_access_in_bounds_and_plan_consistent(checker):
     ("g-stage-swizzle", "G read"),
     ("gt-group-stride", "G^T slot"),
     ("plan-total", "heap-buffer-overflow"),
+    ("cache-z-stride", "logit store"),
 ])
 def test_planted_mistakes_are_caught(checker, plant, sign):
     r = _run(checker, "--plant", plant)
